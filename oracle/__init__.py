@@ -1,0 +1,191 @@
+"""fp64 CPU oracle for the fused attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path
+(``gqa_attention_forward_amd``) never imports, loads or calls it, and it never
+imports the product path: the two share nothing but the seeded input generator.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, libm); this module only
+marshals 16-bit input patterns in and fp64 results out through ctypes.  The C file's
+header states what is computed and which page passages each mode follows:
+
+* ``attn_fwd``            -- the definition of masked softmax attention (page
+  "从零开始写Qwen3", FlashAttention derivation article, sections "简易情况-三矩阵相乘"
+  and "FlashAttention"), with grouped KV heads ``hk = h // (Hq // Hkv)``, causal mask
+  ``j <= i + (N - M)`` and ``lse = m + ln l``;
+* ``attn_fwd_rows``       -- the same definition on a chosen list of rows;
+* ``attn_fwd_blockwise``  -- the page's FlashAttention-2 loop (running max, running
+  denominator, rescaled accumulator, one division after the loop), in fp64;
+* ``attn_fwd_stepnorm``   -- the page's per-step-normalised online-softmax recurrence
+  (section "在线softmax"), in fp64;
+* ``attn_probs``          -- the softmax weight matrix of one (b, h).
+
+Every function is pinned by the ``-m "not gpu"`` tests against closed forms, page
+worked numbers, invariants and an independent library routine.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F16, BF16 = 0, 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.ensure_built()
+        lib = ctypes.CDLL(path)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        ci, cd, cl = ctypes.c_int, ctypes.c_double, ctypes.c_long
+        shape = [ci, ci, ci, ci, ci, ci, ci, cd, ci]  # dtype,B,Hq,Hkv,M,N,D,scale,causal
+        lib.oracle_attn_fwd.argtypes = [u16p, u16p, u16p] + shape + [dp, dp]
+        lib.oracle_attn_fwd_rows.argtypes = [u16p, u16p, u16p] + shape + [i64p, ctypes.c_int64, dp, dp]
+        lib.oracle_attn_fwd_blockwise.argtypes = [u16p, u16p, u16p] + shape + [cl, dp, dp]
+        lib.oracle_attn_fwd_stepnorm.argtypes = [u16p, u16p, u16p] + shape + [cl, dp, dp]
+        lib.oracle_attn_probs.argtypes = [u16p, u16p] + shape + [ci, ci, dp]
+        lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_f16.restype = cd
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_bf16.restype = cd
+        for f in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_attn_fwd_blockwise,
+                  lib.oracle_attn_fwd_stepnorm, lib.oracle_attn_probs):
+            f.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _bits(x) -> np.ndarray:
+    """Raw 16-bit patterns of an fp16/bf16 torch tensor (on the CPU) or a uint16 array."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint16
+        return np.ascontiguousarray(x)
+    import torch
+
+    assert x.dtype in (torch.float16, torch.bfloat16), x.dtype
+    return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def _dtype_code(x) -> int:
+    import torch
+
+    if isinstance(x, np.ndarray):
+        raise TypeError("pass dtype explicitly for raw uint16 arrays")
+    return F16 if x.dtype == torch.float16 else BF16
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(ctypes.POINTER(t))
+
+
+def _shape(q, k, dtype):
+    B, Hq, M, D = q.shape
+    Bk, Hkv, N, Dk = k.shape
+    assert B == Bk and D == Dk
+    return B, Hq, Hkv, M, N, D
+
+
+def _common(q, k, v, dtype):
+    if dtype is None:
+        dtype = _dtype_code(q)
+    B, Hq, Hkv, M, N, D = _shape(q, k, dtype)
+    return dtype, (B, Hq, Hkv, M, N, D), _bits(q), _bits(k), _bits(v)
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool, dtype: int | None = None):
+    """Full forward. Returns (O [B,Hq,M,D] fp64, lse [B,Hq,M] fp64) as numpy arrays."""
+    dtype, (B, Hq, Hkv, M, N, D), qb, kb, vb = _common(q, k, v, dtype)
+    o = np.empty((B, Hq, M, D), np.float64)
+    lse = np.empty((B, Hq, M), np.float64)
+    rc = _load().oracle_attn_fwd(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
+                                 dtype, B, Hq, Hkv, M, N, D, float(scale), int(bool(causal)),
+                                 _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_attn_fwd rejected its arguments")
+    return o, lse
+
+
+def attn_fwd_rows(q, k, v, scale: float, causal: bool, rows, dtype: int | None = None):
+    """Rows given as flat indices (b*Hq + h)*M + i. Returns (O [n,D], lse [n]) fp64."""
+    dtype, (B, Hq, Hkv, M, N, D), qb, kb, vb = _common(q, k, v, dtype)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if rows.size and (rows.min() < 0 or rows.max() >= B * Hq * M):
+        raise ValueError("row index out of range")
+    o = np.empty((rows.size, D), np.float64)
+    lse = np.empty((rows.size,), np.float64)
+    rc = _load().oracle_attn_fwd_rows(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                      _ptr(vb, ctypes.c_uint16), dtype, B, Hq, Hkv, M, N, D, float(scale),
+                                      int(bool(causal)), _ptr(rows, ctypes.c_int64), rows.size,
+                                      _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_attn_fwd_rows rejected its arguments")
+    return o, lse
+
+
+def _online(fn_name, q, k, v, scale, causal, block, dtype):
+    dtype, (B, Hq, Hkv, M, N, D), qb, kb, vb = _common(q, k, v, dtype)
+    o = np.empty((B, Hq, M, D), np.float64)
+    lse = np.empty((B, Hq, M), np.float64)
+    rc = getattr(_load(), fn_name)(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
+                                   dtype, B, Hq, Hkv, M, N, D, float(scale), int(bool(causal)), int(block),
+                                   _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"{fn_name} rejected its arguments")
+    return o, lse
+
+
+def attn_fwd_blockwise(q, k, v, scale: float, causal: bool, block: int, dtype: int | None = None):
+    """The FlashAttention-2 loop in fp64 over blocks of `block` keys (deferred normalisation)."""
+    return _online("oracle_attn_fwd_blockwise", q, k, v, scale, causal, block, dtype)
+
+
+def attn_fwd_stepnorm(q, k, v, scale: float, causal: bool, block: int, dtype: int | None = None):
+    """The per-step-normalised online-softmax recurrence in fp64 over blocks of `block` keys."""
+    return _online("oracle_attn_fwd_stepnorm", q, k, v, scale, causal, block, dtype)
+
+
+def attn_probs(q, k, scale: float, causal: bool, b: int, h: int, dtype: int | None = None):
+    """Softmax weights P [M, N] fp64 of one (b, h)."""
+    if dtype is None:
+        dtype = _dtype_code(q)
+    B, Hq, M, D = q.shape
+    _, Hkv, N, _ = k.shape
+    qb, kb = _bits(q), _bits(k)
+    P = np.empty((M, N), np.float64)
+    rc = _load().oracle_attn_probs(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), dtype, B, Hq, Hkv, M, N,
+                                   D, float(scale), int(bool(causal)), int(b), int(h), _ptr(P, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_attn_probs rejected its arguments")
+    return P
+
+
+def decode(bits: int, dtype: int) -> float:
+    """Decode one 16-bit pattern with the oracle's own decoder."""
+    lib = _load()
+    return lib.oracle_decode_f16(bits) if dtype == F16 else lib.oracle_decode_bf16(bits)
+
+
+def decode_array(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Vectorised over a numpy uint16 array (one ctypes call per element; for tests only)."""
+    lib = _load()
+    f = lib.oracle_decode_f16 if dtype == F16 else lib.oracle_decode_bf16
+    return np.array([f(int(b)) for b in bits.ravel()], dtype=np.float64).reshape(bits.shape)
+
+
+def threads_used() -> int:
+    """OpenMP threads the oracle will use (OMP_NUM_THREADS or the process's CPU affinity)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1

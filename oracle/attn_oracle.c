@@ -1,0 +1,410 @@
+/*
+ * attn_oracle.c -- plain, slow, fp64 CPU oracle for the fused attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file: it exists so that the tests, the smoke check and the benchmark's CPU
+ * baseline can compare the HIP kernels against an independent, obviously correct
+ * implementation.  It shares no code, header, table or constant with the HIP path.
+ *
+ * What it computes (all arithmetic in IEEE double, libm exp/log, index order):
+ *
+ *   Softmax attention written out from its definition, as stated on the page
+ *   "从零开始写Qwen3" (FlashAttention derivation article), section "简易情况-三矩阵相乘"
+ *   (the softmax form of O) and section "FlashAttention" (O_i = sum_j softmax(mask(Q_i K_j^T / sqrt(D))) V_j):
+ *
+ *     for each batch b, query head h:  hk = h / (Hq / Hkv)          (grouped KV head,
+ *         same page, the "pid_kh = pid_qh // groups" mapping in the kernel listing)
+ *       for each query row i:
+ *         visible keys V_i = { j < N : !causal  or  j <= i + (N - M) }
+ *         s_ij = scale * sum_d q[b,h,i,d] * k[b,hk,j,d]
+ *         m_i  = max_{j in V_i} s_ij
+ *         l_i  = sum_{j in V_i} exp(s_ij - m_i)
+ *         O[b,h,i,:] = sum_{j in V_i} exp(s_ij - m_i) / l_i * v[b,hk,j,:]
+ *         lse[b,h,i] = m_i + ln(l_i)
+ *         V_i empty  ->  O row = 0, lse = -inf
+ *
+ *   Readings taken where the pages are silent: the causal mask is aligned to the
+ *   bottom-right corner (j <= i + N - M), which is the pages' "i >= j" when M == N;
+ *   the logsumexp is the natural log over the scaled logits of the visible keys.
+ *
+ * Two further modes run the pages' online-softmax algorithm in fp64, only so that
+ * the tests can check the definition above against it:
+ *   - blockwise: the FlashAttention-2 loop of the same page (section "FlashAttention",
+ *     the kernel listing's running max / running denominator / rescaled
+ *     accumulator, divided by the denominator once after the loop), over blocks of
+ *     `block` visible keys;
+ *   - stepnorm: the per-step-normalised recurrence of section "在线softmax",
+ *     O -> O exp(M_i - M_{i+1}) S_i / S_{i+1} + exp(V' ) / S_{i+1}, applied blockwise.
+ *
+ * Inputs are the raw 16-bit patterns of fp16 (dtype 0) or bf16 (dtype 1) tensors in
+ * contiguous [B,H,rows,D] layout; this file decodes them itself (IEEE 754 binary16,
+ * and bfloat16 = the top half of an IEEE binary32).
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- decoders */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_decode_f16(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int exp = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double mag;
+    if (exp == 0) {
+        mag = ldexp((double)frac, -24); /* subnormal: frac * 2^-10 * 2^-14 */
+    } else if (exp == 31) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        mag = ldexp((double)(frac | 0x400), exp - 25); /* (1 + frac/1024) * 2^(exp-15) */
+    }
+    return sign ? -mag : mag;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_decode_bf16(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int exp = (bits >> 7) & 0xff;
+    int frac = bits & 0x7f;
+    double mag;
+    if (exp == 0) {
+        mag = ldexp((double)frac, -133); /* subnormal: frac * 2^-7 * 2^-126 */
+    } else if (exp == 255) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        mag = ldexp((double)(frac | 0x80), exp - 134); /* (1 + frac/128) * 2^(exp-127) */
+    }
+    return sign ? -mag : mag;
+}
+
+static double *decode_all(const uint16_t *src, size_t n, int dtype)
+{
+    double *dst = (double *)malloc(n * sizeof(double));
+    if (!dst)
+        return NULL;
+    for (size_t i = 0; i < n; ++i)
+        dst[i] = dtype == 0 ? oracle_decode_f16(src[i]) : oracle_decode_bf16(src[i]);
+    return dst;
+}
+
+/* ------------------------------------------------------------ shape helpers */
+
+typedef struct {
+    int B, Hq, Hkv, M, N, D, causal;
+    double scale;
+    const double *q, *k, *v; /* decoded, contiguous [B,H,rows,D] */
+} problem;
+
+/* number of visible keys of query row i: they are exactly j = 0 .. nvis-1 */
+static long visible_count(const problem *p, long i)
+{
+    if (!p->causal)
+        return p->N;
+    long n = i + 1 + (long)p->N - (long)p->M; /* j <= i + N - M  <=>  j < i + 1 + N - M */
+    if (n < 0)
+        n = 0;
+    if (n > p->N)
+        n = p->N;
+    return n;
+}
+
+static const double *q_row(const problem *p, int b, int h, long i)
+{
+    return p->q + (((size_t)b * p->Hq + h) * p->M + i) * p->D;
+}
+
+static const double *k_row(const problem *p, int b, int hk, long j)
+{
+    return p->k + (((size_t)b * p->Hkv + hk) * p->N + j) * p->D;
+}
+
+static const double *v_row(const problem *p, int b, int hk, long j)
+{
+    return p->v + (((size_t)b * p->Hkv + hk) * p->N + j) * p->D;
+}
+
+static double score(const problem *p, const double *qi, const double *kj)
+{
+    double acc = 0.0;
+    for (int d = 0; d < p->D; ++d)
+        acc += qi[d] * kj[d];
+    return p->scale * acc;
+}
+
+/* ------------------------------------------------------ definition, one row */
+
+/* s is scratch of length N. Writes D outputs to o and one lse. */
+static void row_definition(const problem *p, int b, int h, long i, double *s, double *o, double *lse)
+{
+    int hk = h / (p->Hq / p->Hkv);
+    long nv = visible_count(p, i);
+    const double *qi = q_row(p, b, h, i);
+    for (int d = 0; d < p->D; ++d)
+        o[d] = 0.0;
+    if (nv == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    for (long j = 0; j < nv; ++j) {
+        s[j] = score(p, qi, k_row(p, b, hk, j));
+        if (s[j] > m)
+            m = s[j];
+    }
+    double l = 0.0;
+    for (long j = 0; j < nv; ++j)
+        l += exp(s[j] - m);
+    for (long j = 0; j < nv; ++j) {
+        double w = exp(s[j] - m) / l;
+        const double *vj = v_row(p, b, hk, j);
+        for (int d = 0; d < p->D; ++d)
+            o[d] += w * vj[d];
+    }
+    *lse = m + log(l);
+}
+
+/* ------------------------------------- online softmax, blockwise (deferred) */
+
+static void row_blockwise(const problem *p, int b, int h, long i, long block, double *s, double *o, double *lse)
+{
+    int hk = h / (p->Hq / p->Hkv);
+    long nv = visible_count(p, i);
+    const double *qi = q_row(p, b, h, i);
+    for (int d = 0; d < p->D; ++d)
+        o[d] = 0.0; /* the un-normalised accumulator */
+    if (nv == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double run_max = -INFINITY, denom = 0.0;
+    for (long j0 = 0; j0 < nv; j0 += block) {
+        long j1 = j0 + block < nv ? j0 + block : nv;
+        double tile_max = -INFINITY;
+        for (long j = j0; j < j1; ++j) {
+            s[j - j0] = score(p, qi, k_row(p, b, hk, j));
+            if (s[j - j0] > tile_max)
+                tile_max = s[j - j0];
+        }
+        double new_max = run_max > tile_max ? run_max : tile_max;
+        double factor = exp(run_max - new_max); /* exp(-inf) = 0 on the first block */
+        double tile_sum = 0.0;
+        for (int d = 0; d < p->D; ++d)
+            o[d] *= factor;
+        for (long j = j0; j < j1; ++j) {
+            double e = exp(s[j - j0] - new_max);
+            tile_sum += e;
+            const double *vj = v_row(p, b, hk, j);
+            for (int d = 0; d < p->D; ++d)
+                o[d] += e * vj[d];
+        }
+        denom = denom * factor + tile_sum;
+        run_max = new_max;
+    }
+    for (int d = 0; d < p->D; ++d)
+        o[d] /= denom;
+    *lse = run_max + log(denom);
+}
+
+/* ------------------------------ online softmax, normalised after every step */
+
+static void row_stepnorm(const problem *p, int b, int h, long i, long block, double *s, double *o, double *lse)
+{
+    int hk = h / (p->Hq / p->Hkv);
+    long nv = visible_count(p, i);
+    const double *qi = q_row(p, b, h, i);
+    for (int d = 0; d < p->D; ++d)
+        o[d] = 0.0; /* always normalised by the current S */
+    if (nv == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double Mi = -INFINITY, Si = 0.0;
+    for (long j0 = 0; j0 < nv; j0 += block) {
+        long j1 = j0 + block < nv ? j0 + block : nv;
+        double bmax = -INFINITY;
+        for (long j = j0; j < j1; ++j) {
+            s[j - j0] = score(p, qi, k_row(p, b, hk, j));
+            if (s[j - j0] > bmax)
+                bmax = s[j - j0];
+        }
+        double Mn = Mi > bmax ? Mi : bmax;
+        double bsum = 0.0;
+        for (long j = j0; j < j1; ++j)
+            bsum += exp(s[j - j0] - Mn);
+        double Sn = Si * exp(Mi - Mn) + bsum;
+        double keep = exp(Mi - Mn) * Si / Sn; /* factor applied to the old O */
+        for (int d = 0; d < p->D; ++d)
+            o[d] *= keep;
+        for (long j = j0; j < j1; ++j) {
+            double w = exp(s[j - j0] - Mn) / Sn;
+            const double *vj = v_row(p, b, hk, j);
+            for (int d = 0; d < p->D; ++d)
+                o[d] += w * vj[d];
+        }
+        Mi = Mn;
+        Si = Sn;
+    }
+    *lse = Mi + log(Si);
+}
+
+/* ------------------------------------------------------------ entry points */
+
+enum { MODE_DEFINITION = 0, MODE_BLOCKWISE = 1, MODE_STEPNORM = 2 };
+
+/*
+ * Computes the rows listed in `rows` (flat index (b*Hq + h)*M + i), or every row when
+ * rows == NULL (then nrows must be B*Hq*M).  o is [nrows, D] fp64, lse is [nrows] fp64.
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+static int run(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16, int dtype, int B, int Hq,
+               int Hkv, int M, int N, int D, double scale, int causal, const int64_t *rows, int64_t nrows,
+               int mode, long block, double *o, double *lse)
+{
+    if (!q16 || !k16 || !v16 || !o || !lse || B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 || D <= 0)
+        return -1;
+    if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1) || block <= 0)
+        return -1;
+    size_t nq = (size_t)B * Hq * M * D, nk = (size_t)B * Hkv * N * D;
+    problem p;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.M = M;
+    p.N = N;
+    p.D = D;
+    p.causal = causal;
+    p.scale = scale;
+    double *q = decode_all(q16, nq, dtype), *k = decode_all(k16, nk, dtype), *v = decode_all(v16, nk, dtype);
+    if (!q || !k || !v) {
+        free(q);
+        free(k);
+        free(v);
+        return -1;
+    }
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    int64_t total = rows ? nrows : (int64_t)B * Hq * M;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < total; ++r) {
+                int64_t flat = rows ? rows[r] : r;
+                long i = (long)(flat % M);
+                int bh = (int)(flat / M);
+                int b = bh / Hq, h = bh % Hq;
+                if (flat < 0 || b >= B) {
+#pragma omp atomic write
+                    err = 1;
+                    continue;
+                }
+                double *orow = o + (size_t)r * D;
+                if (mode == MODE_DEFINITION)
+                    row_definition(&p, b, h, i, s, orow, lse + r);
+                else if (mode == MODE_BLOCKWISE)
+                    row_blockwise(&p, b, h, i, block, s, orow, lse + r);
+                else
+                    row_stepnorm(&p, b, h, i, block, s, orow, lse + r);
+            }
+            free(s);
+        }
+    }
+    free(q);
+    free(k);
+    free(v);
+    return err ? -1 : 0;
+}
+
+int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype, int B, int Hq, int Hkv,
+                    int M, int N, int D, double scale, int causal, double *o, double *lse)
+{
+    return run(q, k, v, dtype, B, Hq, Hkv, M, N, D, scale, causal, NULL, 0, MODE_DEFINITION, 1, o, lse);
+}
+
+int oracle_attn_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype, int B, int Hq,
+                         int Hkv, int M, int N, int D, double scale, int causal, const int64_t *rows,
+                         int64_t nrows, double *o, double *lse)
+{
+    if (!rows || nrows < 0)
+        return -1;
+    return run(q, k, v, dtype, B, Hq, Hkv, M, N, D, scale, causal, rows, nrows, MODE_DEFINITION, 1, o, lse);
+}
+
+int oracle_attn_fwd_blockwise(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype, int B, int Hq,
+                              int Hkv, int M, int N, int D, double scale, int causal, long block, double *o,
+                              double *lse)
+{
+    return run(q, k, v, dtype, B, Hq, Hkv, M, N, D, scale, causal, NULL, 0, MODE_BLOCKWISE, block, o, lse);
+}
+
+int oracle_attn_fwd_stepnorm(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype, int B, int Hq,
+                             int Hkv, int M, int N, int D, double scale, int causal, long block, double *o,
+                             double *lse)
+{
+    return run(q, k, v, dtype, B, Hq, Hkv, M, N, D, scale, causal, NULL, 0, MODE_STEPNORM, block, o, lse);
+}
+
+/*
+ * The softmax weight matrix P[i][j] of one (b, h): exp(s_ij - m_i) / l_i on visible keys,
+ * exactly 0 on masked ones.  P is [M, N] fp64.  Exposed only so tests can check the
+ * weights themselves (rows sum to one, zeros where masked).
+ */
+int oracle_attn_probs(const uint16_t *q16, const uint16_t *k16, int dtype, int B, int Hq, int Hkv, int M, int N,
+                      int D, double scale, int causal, int b, int h, double *P)
+{
+    if (!q16 || !k16 || !P || b < 0 || b >= B || h < 0 || h >= Hq || Hq % Hkv != 0 || D <= 0)
+        return -1;
+    problem p;
+    memset(&p, 0, sizeof(p));
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.M = M;
+    p.N = N;
+    p.D = D;
+    p.causal = causal;
+    p.scale = scale;
+    double *q = decode_all(q16, (size_t)B * Hq * M * D, dtype), *k = decode_all(k16, (size_t)B * Hkv * N * D, dtype);
+    if (!q || !k) {
+        free(q);
+        free(k);
+        return -1;
+    }
+    p.q = q;
+    p.k = k;
+    int hk = h / (Hq / Hkv);
+    for (long i = 0; i < M; ++i) {
+        double *Pi = P + (size_t)i * N;
+        long nv = visible_count(&p, i);
+        for (long j = 0; j < N; ++j)
+            Pi[j] = 0.0;
+        if (nv == 0)
+            continue;
+        double m = -INFINITY;
+        for (long j = 0; j < nv; ++j) {
+            Pi[j] = score(&p, q_row(&p, b, h, i), k_row(&p, b, hk, j));
+            if (Pi[j] > m)
+                m = Pi[j];
+        }
+        double l = 0.0;
+        for (long j = 0; j < nv; ++j)
+            l += exp(Pi[j] - m);
+        for (long j = 0; j < nv; ++j)
+            Pi[j] = exp(Pi[j] - m) / l;
+    }
+    free(q);
+    free(k);
+    return 0;
+}
