@@ -1,0 +1,150 @@
+"""MI355X (gfx950) fused attention forward: a thin Python binding over libfa.so.
+
+Every step of the computation runs in the HIP kernels of ``csrc/fa_fwd.hip``; this module
+only marshals arguments through the C ABI declared in ``include/fa.h``.  There is no
+fallback: if ``libfa.so`` is missing or cannot be loaded, every call raises.
+
+Functions with the C ABI's names take raw device pointers and sizes:
+
+    fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream)
+    fa_strerror(code), fa_tile_shape(D), fa_tile_counts(...), fa_schedule(...)
+
+and ``attention_forward(q, k, v, causal, scale)`` is the torch-tensor convenience wrapper
+(torch is used only for device memory and the current stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F16, FA_BF16 = 0, 1
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, -1, -2, -3
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {fa_strerror(code)} (code {code})")
+        self.code = code
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m gqa_attention_forward_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ci, cf, cll = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp]
+    lib.fa_fwd.restype = ci
+    lib.fa_strerror.argtypes = [ci]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    ip, llp = ctypes.POINTER(ci), ctypes.POINTER(cll)
+    lib.fa_tile_shape.argtypes = [ci, ip, ip]
+    lib.fa_tile_shape.restype = ci
+    lib.fa_tile_counts.argtypes = [ci, ci, ci, ci, ci, llp, llp, llp]
+    lib.fa_tile_counts.restype = ci
+    lib.fa_schedule.argtypes = [ci, ci, ci, ci, ci, ci, cll, ip, ip, ip]
+    lib.fa_schedule.restype = ci
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes handle of libfa.so (raises if it is not built)."""
+    return _load()
+
+
+# ------------------------------------------------------------- C ABI, by name
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream) -> int:
+    """Raw C ABI call: pointers are integers (device addresses), stream an int or None."""
+    return _load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, M, N, D, float(scale), int(causal), int(dtype), stream)
+
+
+def fa_strerror(code: int) -> str:
+    return _load().fa_strerror(int(code)).decode()
+
+
+def fa_tile_shape(D: int):
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    rc = _load().fa_tile_shape(D, ctypes.byref(bm), ctypes.byref(bn))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_tile_shape")
+    return bm.value, bn.value
+
+
+def fa_tile_counts(M: int, N: int, BM: int, BN: int, causal: bool):
+    """(full, masked, skipped) key tiles of one (b, h)."""
+    f, m, s = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_longlong()
+    rc = _load().fa_tile_counts(M, N, BM, BN, int(bool(causal)), ctypes.byref(f), ctypes.byref(m), ctypes.byref(s))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_tile_counts")
+    return f.value, m.value, s.value
+
+
+def fa_schedule(B: int, Hq: int, Hkv: int, M: int, D: int, causal: bool, wg: int):
+    """(b, h, q_tile) computed by workgroup `wg` of fa_fwd's grid."""
+    b, h, qt = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    rc = _load().fa_schedule(B, Hq, Hkv, M, D, int(bool(causal)), int(wg), ctypes.byref(b), ctypes.byref(h),
+                             ctypes.byref(qt))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_schedule")
+    return b.value, h.value, qt.value
+
+
+# ------------------------------------------------------- torch convenience API
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def attention_forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None):
+    """O, lse = softmax(mask(q k^T * scale)) v for contiguous device tensors
+    q [B,Hq,M,D], k/v [B,Hkv,N,D] (fp16 or bf16).  Returns (o [B,Hq,M,D], lse [B,Hq,M] fp32).
+    The kernel is enqueued on `stream` (default: torch's current stream) and not waited for."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, S, D]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, Hq, M, D = q.shape
+    Bk, Hkv, N, Dk = k.shape
+    if tuple(v.shape) != (Bk, Hkv, N, Dk) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, M), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, M, N, D,
+                scale, causal, _dtype_code(q), stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd")
+    return out, lse
+
+
+__all__ = ["fa_fwd", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+           "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]

@@ -1,0 +1,108 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused attention forward library (libfa.so).
+ *
+ * The operation is exact masked softmax attention with grouped-query KV heads,
+ * computed without materialising the M x N score matrix:
+ *
+ *     O[b,h,i,:] = sum_{j visible to i} softmax_j( scale * q[b,h,i,:] . k[b,hk,j,:] ) * v[b,hk,j,:]
+ *     hk = h / (Hq / Hkv)
+ *     lse[b,h,i] = ln sum_{j visible to i} exp( scale * q[b,h,i,:] . k[b,hk,j,:] )
+ *
+ * Sources (web pages, cited by title and section):
+ *   - "从零开始写Qwen3" (FlashAttention derivation article), sections "在线softmax" and
+ *     "FlashAttention": the online-softmax recurrence, the FlashAttention-2 tiling with
+ *     the KV sequence as the inner loop, the grouped KV head mapping (query head // groups)
+ *     and the causal mask (query index >= key index) of its kernel listing.
+ *   - "从零开始写Qwen3" (FlashAttention speed-up article), sections "改进1-使用正确的grid",
+ *     "改进2-KV只读取下三角", "改进3-两阶段计算", "优化点6-使用exp2而不是exp" and
+ *     "改进点7-把stride当成常量": Q tiles fastest in the grid, KV tiles above the diagonal
+ *     never visited, unmasked tiles separated from the masked diagonal band, exp2 with
+ *     log2(e) folded into the scale, unit stride along the head dimension.
+ *   - "Flash Attention CUDA Kernel 优化: 从 56 到 986 TFLOPS on B300 — G2", section
+ *     "V6: 算术指令优化" ("第一处：推迟 scale 乘法"): scale and max subtraction fused in one
+ *     FMA feeding exp2, valid because scale > 0.
+ *
+ * Readings taken where those pages are silent:
+ *   - causal alignment for M != N is bottom-right: key j is visible to query i iff
+ *     j <= i + (N - M) (the pages' "i >= j" when M == N);
+ *   - a query row that sees no key (causal, M > N) gets O = 0 and lse = -inf;
+ *   - lse is the natural log over the *scaled* logits.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* input/output element type */
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* return codes */
+enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, Hq % Hkv != 0, scale not finite or <= 0,
+                                unknown dtype, sizes whose element counts overflow int64 */
+    FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, or a pointer not 16-byte aligned */
+    FA_ERR_LAUNCH = -3       /* the kernel launch reported an error (hipGetLastError) */
+};
+
+/*
+ * fa_fwd -- fused attention forward on one GPU.
+ *
+ * Arguments (all tensors contiguous, row-major, DEVICE memory owned by the caller):
+ *   q    [B, Hq,  M, D]  fp16 or bf16 (dtype)
+ *   k    [B, Hkv, N, D]  same dtype
+ *   v    [B, Hkv, N, D]  same dtype
+ *   o    [B, Hq,  M, D]  same dtype, written (rounded to nearest even); must not alias q, k, v
+ *   lse  [B, Hq,  M]     fp32, written: natural-log logsumexp of each row's scaled logits
+ *   B, Hq, Hkv, M, N, D  sizes; Hq must be a multiple of Hkv (query head h reads KV head
+ *                        h / (Hq / Hkv)); D must be 64 or 128
+ *   scale                > 0 and finite (usually 1/sqrt(D))
+ *   causal               0: every key visible; nonzero: key j visible to query i iff j <= i + N - M
+ *   dtype                FA_F16 or FA_BF16
+ *   stream               a hipStream_t, or NULL for the default stream
+ *
+ * All pointers must be 16-byte aligned.  Indexing is 64-bit.
+ *
+ * Behaviour: validates every argument before any HIP call and returns a negative code
+ * without touching the GPU if one is bad.  Otherwise enqueues one kernel on `stream`
+ * and returns FA_OK without synchronising; the library allocates nothing, frees nothing
+ * and keeps no global mutable state, so concurrent calls on different streams are safe.
+ * Device faults surface at the caller's next synchronisation, as for any HIP kernel.
+ * The result is deterministic: the same inputs give the same bits on every call.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M, int N,
+           int D, float scale, int causal, int dtype, void *stream);
+
+/* Human-readable text for a return code (static storage; never NULL). */
+const char *fa_strerror(int code);
+
+/*
+ * Introspection of the launch plan (host-only, no GPU needed).  These report the tiling
+ * fa_fwd uses, so that tests can check the tile classification against the pages' worked
+ * counts and benchmarks can count the work actually issued.
+ *
+ * fa_tile_shape: the query-tile and key-tile heights fa_fwd uses for head dimension D.
+ *   Returns FA_OK, or FA_ERR_UNSUPPORTED for an unsupported D.
+ *
+ * fa_tile_counts: for one (b, h), with query tiles of BM rows and key tiles of BN rows,
+ *   counts the key tiles visited without a mask (*full), with a mask (*masked: the
+ *   diagonal band of the causal mask and a ragged last key tile), and skipped (*skipped:
+ *   tiles that no row of the query tile can see, never loaded).
+ *   Follows "从零开始写Qwen3" (FlashAttention speed-up article), sections "改进2-KV只读取下三角"
+ *   and "改进3-两阶段计算".  Returns FA_OK or FA_ERR_INVALID_ARG.
+ *
+ * fa_schedule: the (b, h, query-tile) that workgroup `wg` of fa_fwd's grid computes,
+ *   for a launch of B * Hq * ceil(M / BM) workgroups.  Returns FA_OK or FA_ERR_INVALID_ARG.
+ */
+int fa_tile_shape(int D, int *BM, int *BN);
+int fa_tile_counts(int M, int N, int BM, int BN, int causal, long long *full, long long *masked,
+                   long long *skipped);
+int fa_schedule(int B, int Hq, int Hkv, int M, int D, int causal, long long wg, int *b, int *h, int *q_tile);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,114 @@
+"""Parity of the HIP kernels (through the C ABI) against the fp64 CPU oracle, element by element.
+
+Tolerances: max-abs error of O <= 4e-3 (fp16) / 1.6e-2 (bf16); logsumexp within 1e-3.
+Rows that see no key must give O = 0 exactly and lse = -inf.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_forward_amd as fa
+import oracle
+from gqa_attention_forward_amd.inputs import WORKLOADS, make_custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float16: 4e-3, torch.bfloat16: 1.6e-2}
+LSE_TOL = 1e-3
+
+
+def _run_gpu(q, k, v, causal, scale):
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o, lse = fa.attention_forward(dq, dk, dv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
+    o_gpu = o_gpu.double().numpy()
+    lse_gpu = lse_gpu.double().numpy()
+    fin = np.isfinite(lse_ref)
+    err = np.abs(o_gpu - o_ref).max() if o_ref.size else 0.0
+    lerr = np.abs(lse_gpu[fin] - lse_ref[fin]).max() if fin.any() else 0.0
+    print(f"{what}: max|dO| = {err:.3e} (tol {TOL[dtype]:.1e}), max|dlse| = {lerr:.3e}", flush=True)
+    assert np.all(np.isfinite(o_gpu)), what
+    assert err <= TOL[dtype], what
+    assert lerr <= LSE_TOL, what
+    # rows without a visible key
+    assert np.all(np.isneginf(lse_gpu[~fin])), what
+    assert np.all(o_gpu[~fin] == 0.0), what
+
+
+SMALL = [
+    # B, Hq, Hkv, M, N, D, causal, dtype        (several tiles, ragged tails, M != N both ways)
+    (1, 2, 1, 128, 128, 64, True, torch.float16),
+    (2, 4, 2, 300, 300, 128, True, torch.bfloat16),
+    (1, 8, 2, 77, 300, 128, True, torch.float16),
+    (1, 4, 1, 300, 77, 128, True, torch.bfloat16),      # first 223 rows see no key
+    (2, 2, 2, 200, 333, 128, False, torch.float16),
+    (1, 4, 4, 129, 65, 64, False, torch.bfloat16),
+    (1, 6, 3, 256, 1000, 64, True, torch.bfloat16),
+    (3, 2, 1, 1, 1, 128, True, torch.float16),           # one query, one key
+    (1, 2, 1, 1, 500, 128, True, torch.float16),         # decode-like: one query row
+    (1, 2, 2, 64, 64, 128, False, torch.bfloat16),       # a single half-filled query tile
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(str(x) for x in s[:7]) + str(s[7])[-4:])
+def test_small_shapes_full_compare(shape):
+    B, Hq, Hkv, M, N, D, causal, dtype = shape
+    q, k, v = make_custom(B, Hq, Hkv, M, N, D, dtype, seed=M * 7 + N)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = _run_gpu(q, k, v, causal, scale)
+    ro, rlse = oracle.attn_fwd(q, k, v, scale, causal)
+    _check(o, lse, ro, rlse, dtype, f"shape {shape}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_peaky_keys_small(dtype):
+    """Peaky logits (10% of K rows x8) exercise the running-max rescale."""
+    q, k, v = make_custom(1, 4, 1, 512, 512, 128, dtype, seed=99, peak_rate=0.1)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _run_gpu(q, k, v, True, scale)
+    ro, rlse = oracle.attn_fwd(q, k, v, scale, True)
+    _check(o, lse, ro, rlse, dtype, "peaky")
+
+
+def _sample_rows(w, rng_seed=0, n_random=512):
+    """Flat row indices: the first 64 and last 64 rows of every (b, h), and random rows."""
+    rows = []
+    for bh in range(w.B * w.Hq):
+        base = bh * w.M
+        rows.extend(range(base, base + min(64, w.M)))
+        rows.extend(range(base + max(0, w.M - 64), base + w.M))
+    rng = np.random.default_rng(rng_seed)
+    rows.extend(rng.integers(0, w.B * w.Hq * w.M, size=n_random).tolist())
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(name):
+    """Every workload at its full size, in the same launch configuration the benchmark times.
+    The two small workloads are compared in full; the large ones on sampled rows (the oracle
+    computes those rows one by one), plus whole-tensor properties."""
+    w = WORKLOADS[name]
+    q, k, v, n_peaky = make_inputs(w)
+    print(f"{name}: {w}, peaky rows {n_peaky}", flush=True)
+    o, lse = _run_gpu(q, k, v, w.causal, w.scale)
+    assert torch.isfinite(o.float()).all()
+    full = w.B * w.Hq * w.M * w.N <= 64 * 1024 * 1024
+    if full:
+        ro, rlse = oracle.attn_fwd(q, k, v, w.scale, w.causal)
+        _check(o, lse, ro, rlse, w.dtype, name)
+        return
+    rows = _sample_rows(w, rng_seed=w.seed, n_random=256 if w.N >= 8192 else 512)
+    if w.B * w.Hq > 64:  # keep the oracle's share to seconds: the first/last rows of a subset of heads
+        keep = rows % (w.B * w.Hq * w.M) < 64 * w.M
+        extra = _sample_rows(w, rng_seed=w.seed + 1, n_random=512)
+        rows = np.unique(np.concatenate([rows[keep], extra[-512:]]))
+    ro, rlse = oracle.attn_fwd_rows(q, k, v, w.scale, w.causal, rows)
+    og = o.reshape(-1, w.D)[torch.from_numpy(rows)]
+    lg = lse.reshape(-1)[torch.from_numpy(rows)]
+    _check(og, lg, ro, rlse, w.dtype, f"{name} ({rows.size} sampled rows)")
