@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+
+One step is one fa_fwd call over the whole workload (inputs resident in HBM).  The default
+workload is the long causal GQA prefill (B=1, Hq=32, Hkv=8, M=N=16384, D=128, bf16, 1% of
+K rows scaled by 8).  Prints ONE JSON line on stdout:
+
+  value     causal-adjusted TFLOPS = 4*D*(visible query/key pairs)*B*Hq / (wall time per step)
+  roofline  the kernel's average duration from HIP events recorded around every timed launch
+            on the launch stream, against the dense bf16/fp16 MFMA peak (2500 TFLOP/s); plus
+            HBM traffic per launch from the committed rocprofv3 counter summary, or null when
+            the kernel source changed since the counters were taken
+  cpu_baseline  the fp64 CPU oracle timed on a bounded random sample of the same workload's
+            rows, in the same unit
+
+``--all`` also prints one line per workload to stderr (not part of the contract).
+``--calibrate-copy BYTES`` runs only a plain device-to-device copy of BYTES bytes (used to
+scale the FETCH_SIZE / WRITE_SIZE counters of the profiles).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "gqa_attention_forward_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_long_causal_gqa_16k_traffic.md")
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal_gqa_16k")
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch recorded in the committed counter summary, if it matches the
+    current kernel source."""
+    if workload != "long_causal_gqa_16k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def time_gpu(fa, w, q, k, v, steps, warmup):
+    import torch
+
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.M), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
+    return wall, durs, o, lse
+
+
+def cpu_baseline(w, q, k, v, target_s):
+    """Times the oracle (as it stands) on a random sample of rows of the workload."""
+    import numpy as np
+
+    import oracle
+    from gqa_attention_forward_amd import accounting
+
+    total_rows = w.B * w.Hq * w.M
+    rng = np.random.default_rng(1234)
+
+    def flops_of(rows):
+        i = rows % w.M
+        if w.causal:
+            vis = np.clip(i + 1 + (w.N - w.M), 0, w.N)
+        else:
+            vis = np.full(rows.shape, w.N)
+        return float(4 * w.D * vis.sum())
+
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    # each oracle call decodes the whole inputs first (a fixed cost); time two probe sizes,
+    # fit time = fixed + flops / rate, then size the timed sample to about target_s seconds
+    times = []
+    for n_probe in (64, 512):
+        probe = rng.integers(0, total_rows, size=n_probe).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attn_fwd_rows(qc, kc, vc, w.scale, w.causal, probe)
+        times.append((flops_of(probe), time.perf_counter() - t0))
+    (f1, t1), (f2, t2) = times
+    per_flop = max((t2 - t1) / max(f2 - f1, 1.0), 1e-15)
+    fixed = max(t1 - f1 * per_flop, 0.0)
+    avg_row = accounting.causal_adjusted_flops(1, 1, w.M, w.N, w.D, w.causal) / w.M
+    n = int(min(total_rows, max(256, (target_s - fixed) / per_flop / avg_row)))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd_rows(qc, kc, vc, w.scale, w.causal, rows)
+    dt = time.perf_counter() - t0
+    fl = flops_of(rows)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.threads_used(),
+        "kind": "oracle",
+        "sample": f"{n} random query rows (of {total_rows}) of {w.name}, all their visible keys; "
+                  f"{fl / 1e9:.1f} GFLOP causal-adjusted in {dt:.1f} s, fp64",
+    }
+
+
+def calibrate_copy(nbytes: int):
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}))
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward of this library runs on a single "
+              "device (no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    import torch
+
+    import gqa_attention_forward_amd as fa
+    from gqa_attention_forward_amd import accounting
+    from gqa_attention_forward_amd.inputs import WORKLOADS, WORKLOAD_ORDER, make_inputs
+
+    if not os.path.exists(fa.LIB_PATH):
+        from gqa_attention_forward_amd import build as hip_build
+
+        hip_build.build()
+
+    names = WORKLOAD_ORDER if args.all else [args.workload]
+    result = None
+    for name in names:
+        w = WORKLOADS[name]
+        q, k, v, _ = make_inputs(w, device="cuda")
+        torch.cuda.synchronize()
+        wall, durs, o, lse = time_gpu(fa, w, q, k, v, args.steps, args.warmup)
+        flops = accounting.workload_flops(w)
+        tflops = flops * args.steps / wall / 1e12
+        avg_ms = sum(durs) / len(durs)
+        achieved = flops / (avg_ms * 1e-3) / 1e12
+        bm, bn = fa.fa_tile_shape(w.D)
+        f_, m_, _ = fa.fa_tile_counts(w.M, w.N, bm, bn, w.causal)
+        issued = 4 * bm * bn * w.D * (f_ + m_) * w.B * w.Hq
+        line = {
+            "workload": name, "tflops": round(tflops, 2), "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "kernel_median_us": round(durs[len(durs) // 2] * 1e3, 2), "kernel_min_us": round(durs[0] * 1e3, 2),
+            "pct_mfma_peak": round(100 * achieved / MFMA_PEAK_TFLOPS, 2),
+            "issued_mfma_tflops": round(issued / (avg_ms * 1e-3) / 1e12, 2),
+            "compulsory_gbs": round(accounting.workload_bytes(w) / (avg_ms * 1e-3) / 1e9, 1),
+        }
+        print(json.dumps(line), file=sys.stderr, flush=True)
+        if name == args.workload:
+            assert torch.isfinite(o.float()).all().item(), "non-finite output"
+            traffic = read_traffic(name)
+            result = {
+                "metric": "attention fwd TFLOPS (causal-adjusted) and % of MI355X FP16/BF16 MFMA peak",
+                "value": round(tflops, 3),
+                "unit": "TFLOPS",
+                "n_gpus": 1,
+                "steps": args.steps,
+                "warmup": args.warmup,
+                "ms_per_step": round(wall / args.steps * 1e3, 4),
+                "higher_is_better": True,
+                "scaling": "weak",
+                "vs_baseline": None,
+                "dtype": "bf16" if w.dtype == torch.bfloat16 else "f16",
+                "data": "synthetic",
+                "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "M": w.M, "N": w.N, "D": w.D,
+                           "causal": w.causal, "seed": w.seed, "peaky_k_rows": w.peak_rate,
+                           "parallelism": "single GPU"},
+                "pct_of_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 3),
+                "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                             "traffic": traffic,
+                             "kernel_avg_us": round(avg_ms * 1e3, 3)},
+                "cpu_baseline": None,
+            }
+            if not args.no_cpu_baseline:
+                result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

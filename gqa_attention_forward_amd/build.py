@@ -40,6 +40,10 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # a shared library links even with unresolved symbols: resolve them all now, loudly
+    import ctypes
+
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     return LIB
 

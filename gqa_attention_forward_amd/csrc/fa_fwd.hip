@@ -40,10 +40,14 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kBN = 64;       // keys per tile
@@ -63,9 +67,8 @@ template <> struct Elem<_Float16> {
     // round-to-nearest-even fp32 -> fp16, two values packed in one dword (x in the low half)
     static __device__ __forceinline__ unsigned pack2(float x, float y)
     {
-        _Float16 hx = (_Float16)x, hy = (_Float16)y;
-        return (unsigned)__builtin_bit_cast(unsigned short, hx) |
-               ((unsigned)__builtin_bit_cast(unsigned short, hy) << 16);
+        const f32x2 v = {x, y};
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
     }
 };
 
@@ -77,38 +80,42 @@ template <> struct Elem<__bf16> {
     }
     static __device__ __forceinline__ unsigned pack2(float x, float y)
     {
-        __bf16 bx = (__bf16)x, by = (__bf16)y;
-        return (unsigned)__builtin_bit_cast(unsigned short, bx) |
-               ((unsigned)__builtin_bit_cast(unsigned short, by) << 16);
+        const f32x2 v = {x, y};
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
     }
 };
+
+// 16 bytes per lane from a buffer straight into LDS: lane i writes dst + 16 i (dst is uniform).
+// The builtin only exists for the device; the host pass never sees the call.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, lds_void *dst, unsigned voffset)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voffset, 0, 0, 0);
+#endif
+}
 
 // ------------------------------------------------------------------- layouts
 
 // Row permutation of a 32-row MFMA operand block: A-operand row i holds key (or output
 // column) pi(i), chosen so that accumulator register r of a lane in half hh maps to
-// 16*hh + r.  (Accumulator row of register r in half hh is 8*(r/4) + 4*hh + r%4.)
-__device__ __forceinline__ int pi32(int i) { return 16 * ((i >> 2) & 1) + ((i >> 3) << 2) + (i & 3); }
+// 16*hh + r.  (The accumulator row of register r in half hh is 8*(r/4) + 4*hh + r%4.)
+// pi_inv is that accumulator-row formula itself.
+__host__ __device__ constexpr int pi32(int i) { return 16 * ((i >> 2) & 1) + ((i >> 3) << 2) + (i & 3); }
+__host__ __device__ constexpr int pi32_inv(int k) { return ((k & 15) >> 2) * 8 + 4 * (k >> 4) + (k & 3); }
 
-// LDS tiles are row-major [BN][D] in 16-byte units, XOR-swizzled per row so that the
-// 16 lanes served together by one LDS pass hit 16 distinct 16-byte bank groups (gfx950
-// LDS: 64 banks of 4 bytes).
-template <int D> __device__ __forceinline__ int swz_k(int row, int unit)
-{
-    if constexpr (D == 128)  // MFMA A-operand reads touch rows pi(0..15): bits 0,1,4,2 distinguish them
-        return unit ^ ((row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3));
-    else  // 128-byte rows: two rows share a 256-byte bank window, the row's parity separates them
-        return unit ^ (((row >> 1) & 1) | (((row >> 4) & 1) << 1) | (((row >> 2) & 1) << 2));
-}
-
-template <int D> __device__ __forceinline__ int swz_v(int row, int unit)
-{
-    // transposing reads touch 4 consecutive rows x units {u, u+2}: rows' low bits pick disjoint unit pairs
-    if constexpr (D == 128)
-        return unit ^ ((row & 1) | (((row >> 1) & 1) << 2));
-    else
-        return unit ^ ((row >> 1) & 1);
-}
+// LDS tiles.  gfx950 LDS has 64 banks of 4 bytes; a 16-byte read serves 16 lanes per pass,
+// the 8-byte transposing read 32 lanes per pass.  Rows are padded so that every pass of
+// the MFMA operand reads and of the tile writes touches distinct banks, and so that every
+// read address is a per-lane base plus a compile-time offset:
+//   K tile: the rows of each 32-key block are stored in pi order (slot i holds key pi(i)), so
+//     the 16 lanes of a pass read 16 consecutive slots; a pitch of (odd) 16-byte units spreads
+//     them over all 16 bank groups.
+//   V tile: row-major in key order; a transposing pass reads 4 consecutive rows x 4 units, so
+//     the pitch shifts consecutive rows by 4 bank groups.
+template <int D> struct Lds {
+    static constexpr int K_PITCH = D == 128 ? 17 * 16 : 9 * 16;   // bytes
+    static constexpr int V_PITCH = D == 128 ? 20 * 16 : 12 * 16;  // bytes
+};
 
 struct Params {
     const void *q, *k, *v;
@@ -126,15 +133,14 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
 {
     constexpr int UNITS = D / 8;                       // 16-byte units per row
-    constexpr int ROWB = D * 2;                        // bytes per row
-    constexpr int TILE_BYTES = kBN * ROWB;             // one K or V tile
-    constexpr int LOADS = kBN * UNITS / kThreads;      // 16-byte global loads per thread per tile
     constexpr int KS = D / 16;                         // MFMA k-steps over the head dimension
     constexpr int KB = kBN / 32;                       // 32-key blocks per tile
     constexpr int DB = D / 32;                         // 32-column blocks of the output
-    static_assert(LOADS * kThreads == kBN * UNITS, "tile must split evenly over the threads");
+    constexpr int KP = Lds<D>::K_PITCH, VP = Lds<D>::V_PITCH;
+    constexpr int K_TILE = kBN * KP, V_TILE = kBN * VP;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * 2 * TILE_BYTES];
+    // [K buf 0 | K buf 1 | V buf 0 | V buf 1]
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * K_TILE + 2 * V_TILE];
     lds_u8 *smem = (lds_u8 *)smem_raw;
 
     const int tid = threadIdx.x;
@@ -167,32 +173,62 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         qreg[ks] = qvalid ? *(const u32x4 *)(qg + (size_t)qrow * D + ks * 16 + hh * 8) : z;
     }
 
-    // ---- A3: global -> register -> LDS staging of one K tile and one V tile
-    u32x4 kst[LOADS], vst[LOADS];
-    auto load_tile = [&](int t) {
-        const int n0 = t * kBN;
+    // ---- A3: K and V tiles go from HBM straight into LDS: buffer loads whose destination is
+    // LDS, 16 bytes per lane, lane i of one instruction filling bytes [16 i, 16 i + 16) of a
+    // 1 KiB block.  Instruction j of a tile fills block j of that tile's LDS buffer; the wave
+    // issues j = wave, wave + 4, ...  Each tile gets its own buffer resource whose size ends at
+    // N, so key rows past N -- and the lanes that land on pad units, given an offset past any
+    // size -- read as zero without touching memory.
+    constexpr int K_INSTR = K_TILE / 1024, V_INSTR = V_TILE / 1024;
+    static_assert(K_INSTR * 1024 == K_TILE && V_INSTR * 1024 == V_TILE, "tiles are whole 1 KiB blocks");
+    constexpr int KI = (K_INSTR + kWaves - 1) / kWaves, VI = (V_INSTR + kWaves - 1) / kWaves;
+    constexpr unsigned kPad = 0x7fffff00u;  // an offset past the end of every tile resource
+    constexpr int TILE_GBYTES = kBN * D * (int)sizeof(T);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const long long kv_bytes = (long long)N * D * (long long)sizeof(T);
+    unsigned k_src[KI], v_src[VI];
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int c = j * kThreads + tid;
-            const int row = c / UNITS, unit = c % UNITS;
-            const bool ok = n0 + row < N;
-            const size_t off = (size_t)(n0 + row) * D + unit * 8;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kst[j] = ok ? *(const u32x4 *)(kg + off) : z;
-            vst[j] = ok ? *(const u32x4 *)(vg + off) : z;
+    for (int i = 0; i < KI; ++i) {
+        const int u = (wave_u + kWaves * i) * 64 + lane;  // 16-byte unit of the K tile this lane fills
+        const int slot = u / (KP / 16), unit = u % (KP / 16);
+        const int key = (slot & ~31) | pi32(slot & 31);    // slot order pi inside each 32-key block
+        k_src[i] = unit < UNITS ? (unsigned)(key * D * (int)sizeof(T) + unit * 16) : kPad;
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+        const int u = (wave_u + kWaves * i) * 64 + lane;
+        const int row = u / (VP / 16), unit = u % (VP / 16);
+        v_src[i] = unit < UNITS ? (unsigned)(row * D * (int)sizeof(T) + unit * 16) : kPad;
+    }
+    auto tile_rsrc = [&](const T *base, int t) {
+        const long long off = (long long)t * TILE_GBYTES;
+        const long long rem = kv_bytes - off;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + off), (short)0,
+                                                 (int)(rem > 0 ? (rem < TILE_GBYTES ? rem : TILE_GBYTES) : 0),
+                                                 0x00020000);
+    };
+    auto load_k = [&](int t, int buf) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, t);
+        lds_u8 *dst = smem + buf * K_TILE;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            const int j = wave_u + kWaves * i;
+            if (K_INSTR % kWaves == 0 || j < K_INSTR)
+                lds_load16(rs, (lds_void *)(dst + j * 1024), k_src[i]);
         }
     };
-    auto store_tile = [&](int buf) {
-        lds_u8 *kb = smem + buf * 2 * TILE_BYTES;
-        lds_u8 *vb = kb + TILE_BYTES;
+    auto load_v = [&](int t, int buf) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, t);
+        lds_u8 *dst = smem + 2 * K_TILE + buf * V_TILE;
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int c = j * kThreads + tid;
-            const int row = c / UNITS, unit = c % UNITS;
-            *(lds_u32x4 *)(kb + row * ROWB + swz_k<D>(row, unit) * 16) = kst[j];
-            *(lds_u32x4 *)(vb + row * ROWB + swz_v<D>(row, unit) * 16) = vst[j];
+        for (int i = 0; i < VI; ++i) {
+            const int j = wave_u + kWaves * i;
+            if (V_INSTR % kWaves == 0 || j < V_INSTR)
+                lds_load16(rs, (lds_void *)(dst + j * 1024), v_src[i]);
         }
     };
+    // this wave's loads into LDS have landed (vmcnt(0)); a barrier then publishes them
+    auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
     // ---- online-softmax state (A6) and output accumulator
     f32x16 oacc[DB];
@@ -205,120 +241,184 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
     const float c = p.c;
     const int causal_lim = qrow + (N - M);  // last visible key of this row (causal)
 
-    // per-lane constant parts of the LDS addresses
-    const int krow_in_blk = pi32(ql);
-    // transposing V read: source lane (e_src, j) of a 16-lane group supplies 4 columns
+    // per-lane read bases: K slot ql of each 32-key block, unit hh of each 32-byte k-step
+    const int k_rd = ql * KP + hh * 16;
+    // transposing V read: in each 16-lane group, source lane 4*e + j reads row (4-row group base + e)
+    // at column chunk dcol(j); the result gives lane l the 4 keys of column pi(l % 32)
     const int tr_g = (lane >> 4) & 1, tr_s = lane & 15, tr_e = tr_s >> 2, tr_j = tr_s & 3;
-    const int tr_dcol = 16 * (tr_j & 1) + 8 * tr_g + 4 * (tr_j >> 1);  // column offset inside a 32-column block
+    const int tr_dcol = 16 * (tr_j & 1) + 8 * tr_g + 4 * (tr_j >> 1);
+    const int v_rd = (hh * 16 + tr_e) * VP + tr_dcol * 2;
 
-    const int n_tiles = kr.n_tiles;
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
+    // The loop body is written as two straight-line phases whose MFMAs are interleaved with
+    // the VALU work of the softmax (the MFMA pipe runs while the wave issues VALU instructions):
+    //   phase 1: S_{t+1} = K_{t+1} Q^T (MFMA)   ||  p = exp2(fma(s, c, -m c)) of tile t, row sums, rounding
+    //   phase 2: O^T += V_t^T P_t^T    (MFMA)   ||  mask and row max of tile t+1
+    // followed, only when some row's running max grew, by the rescale of O.  The order inside
+    // a phase is fixed with scheduling barriers: MFMA i, then its share of VALU work, with the
+    // LDS operands of MFMA i+2 read ahead.
+    constexpr int NM = KS * KB;                 // MFMAs per phase
+    constexpr int PAIRS = KB * 8;               // probability pairs per lane per tile
+    constexpr int PPM = PAIRS / NM;             // pairs per MFMA in phase 1
+    static_assert(PPM * NM == PAIRS, "phase 1 must split evenly");
+    static_assert(NM == KB * 2 * DB, "phase 2 has as many MFMAs as phase 1");
 
-    for (int t = 0; t < n_tiles; ++t) {
-        if (t + 1 < n_tiles) load_tile(t + 1);  // in flight during this tile's math
-        const lds_u8 *kb_lds = smem + (t & 1) * 2 * TILE_BYTES;
-        const lds_u8 *vb_lds = kb_lds + TILE_BYTES;
+    // one pair of probabilities: exp2 of the scaled, max-shifted scores, summed and rounded to T
+    auto prob_pair = [&](const f32x16 (&s_cur)[KB], int pi, float mc, unsigned (&pk)[KB][8], float &psum) {
+        const int pkb = pi / 8, pr = (pi % 8) * 2;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[pkb][pr], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[pkb][pr + 1], c, -mc));
+        psum += p0 + p1;
+        pk[pkb][pr / 2] = Elem<T>::pack2(p0, p1);
+    };
+
+    // ---- A4 (+A6 of the previous tile): scores of the tile in `kbuf`, interleaved with the
+    // probabilities of `s_cur` given the row max scaled by c (mc)
+    auto phase1 = [&](int kbuf, f32x16 (&s_next)[KB], const f32x16 (&s_cur)[KB], float mc,
+                      unsigned (&pk)[KB][8], float &psum) {
+        const lds_u8 *src = smem + kbuf * K_TILE + k_rd;
+        auto rd = [&](int i) { return *(const lds_u32x4 *)(src + (i % KB) * 32 * KP + (i / KB) * 32); };
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.f;
+        u32x4 a[3];
+        a[0] = rd(0);
+        a[1] = rd(1);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            if (i + 2 < NM) a[(i + 2) % 3] = rd(i + 2);
+            s_next[i % KB] = Elem<T>::mfma(a[i % 3], qreg[i / KB], s_next[i % KB]);
+#pragma unroll
+            for (int j = 0; j < PPM; ++j) prob_pair(s_cur, i * PPM + j, mc, pk, psum);
+            asm volatile("" : "+v"(psum));  // keep the row-sum chain in this phase
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // probabilities of the last tile, with no next tile to overlap
+    auto probs = [&](const f32x16 (&s_cur)[KB], float mc, unsigned (&pk)[KB][8], float &psum) {
+#pragma unroll
+        for (int pi = 0; pi < PAIRS; ++pi) prob_pair(s_cur, pi, mc, pk, psum);
+    };
+
+    // ---- A5: visibility of key `key` to this lane's row (diagonal band / ragged last tile)
+    auto visible = [&](int key) { return key < N && (!CAUSAL || key <= causal_lim); };
+
+    // mask (unless `none`) the scores of tile t, then return their in-lane max
+    auto mask_max = [&](int t, f32x16 (&sc)[KB], bool none = false) {
         const int n0 = t * kBN;
-
-        // ---- A4: S^T = K Q^T, fp32 accumulate; lane holds keys n0 + 32*kb + 16*hh + r of row qrow
-        f32x16 s[KB];
+        float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int row = kb * 32 + krow_in_blk;
-                const u32x4 a = *(const lds_u32x4 *)(kb_lds + row * ROWB + swz_k<D>(row, 2 * ks + hh) * 16);
-                s[kb] = Elem<T>::mfma(a, qreg[ks], s[kb]);
+            for (int r = 0; r < 16; ++r) {
+                if (!none) sc[kb][r] = visible(n0 + kb * 32 + hh * 16 + r) ? sc[kb][r] : -INFINITY;
+                mt = fmaxf(mt, sc[kb][r]);
             }
-        }
+        return mt;
+    };
 
-        // ---- A5: mask on the diagonal band and on a ragged last tile only
-        if (t >= kr.n_full) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = n0 + kb * 32 + hh * 16 + r;
-                    const bool vis = key < N && (!CAUSAL || key <= causal_lim);
-                    s[kb][r] = vis ? s[kb][r] : -INFINITY;
-                }
-        }
-
-        // ---- A6: online softmax for this tile
-        float mt = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-        {
-            // the other half of the row lives in lane ^ 32
-            auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mt),
-                                                       __builtin_bit_cast(unsigned, mt), false, false);
-            mt = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
-        }
+    // ---- A6: cross-half row max and running-max update.  O and the partial sum are rescaled only
+    // when some row's max grew (alpha = exp2((m_old - m_new) * c) is exactly 1 otherwise);
+    // returns m * c for the exp2 of the tile
+    auto update_max = [&](float mt) {
+        auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mt), __builtin_bit_cast(unsigned, mt),
+                                                   false, false);
+        mt = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
         const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet: keep exp2 finite
-        const float mc = m_use * c;
-        const float alpha = __builtin_amdgcn_exp2f(m_run * c - mc);  // 0 on the first visible tile
-        m_run = m_new;
-
-        float psum = 0.f;
-        unsigned pk[KB][8];  // probabilities rounded to T, two per dword, in key order
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -mc));
-                psum += p0 + p1;
-                pk[kb][r / 2] = Elem<T>::pack2(p0, p1);
-            }
-        l_part = l_part * alpha + psum;
-        if (__any(alpha != 1.f)) {
+        const bool grew = m_new > m_run;
+        if (__any(grew)) {
+            const float alpha = grew ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;  // 0 from -inf
+            l_part *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
         }
+        return (m_run == -INFINITY ? 0.f : m_run) * c;  // no visible key yet: keep exp2 finite
+    };
 
-        // ---- A7: O^T += V^T P^T; P is the B operand straight from registers
+    // ---- A7: O^T += V^T P^T (P is the B operand straight from registers), interleaved with
+    // the mask (MASK) and in-lane row max of the next tile's scores s_next (first key n0)
+    auto phase2 = [&](int vbuf, const unsigned (&pk)[KB][8], const f32x16 (&s_next)[KB]) {
+        const lds_u8 *src = smem + 2 * K_TILE + vbuf * V_TILE + v_rd;
+        // MFMA i: key block kb = i / (2*DB), key octet tt = (i / DB) % 2, column block db = i % DB
+        auto rd = [&](int i) {
+            const int kb = i / (2 * DB), tt = (i / DB) % 2, db = i % DB;
+            const int off = (kb * 32 + tt * 8) * VP + db * 64;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(src + off));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(src + off + 4 * VP));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
+            return v;
+        };
+        constexpr int VPM = KB * 16 / NM;  // score values of s_next handled per MFMA
+        float mt = -INFINITY;
+        u32x4 a[3];
+        a[0] = rd(0);
+        a[1] = rd(1);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int i = 0; i < NM; ++i) {
+            if (i + 2 < NM) a[(i + 2) % 3] = rd(i + 2);
+            const int kb = i / (2 * DB), tt = (i / DB) % 2;
+            const u32x4 bop = {pk[kb][4 * tt], pk[kb][4 * tt + 1], pk[kb][4 * tt + 2], pk[kb][4 * tt + 3]};
+            oacc[i % DB] = Elem<T>::mfma(a[i % 3], bop, oacc[i % DB]);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                u32x4 bop = {pk[kb][4 * tt], pk[kb][4 * tt + 1], pk[kb][4 * tt + 2], pk[kb][4 * tt + 3]};
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    i16x4 lo, hi;
-                    {
-                        const int row = kb * 32 + hh * 16 + tt * 8 + tr_e;  // keys k0 .. k0+3
-                        const int col = db * 32 + tr_dcol;
-                        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)(vb_lds + row * ROWB + swz_v<D>(row, col >> 3) * 16 + (col & 7) * 2));
-                    }
-                    {
-                        const int row = kb * 32 + hh * 16 + tt * 8 + 4 + tr_e;  // keys k0+4 .. k0+7
-                        const int col = db * 32 + tr_dcol;
-                        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)(vb_lds + row * ROWB + swz_v<D>(row, col >> 3) * 16 + (col & 7) * 2));
-                    }
-                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-                    const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                    oacc[db] = Elem<T>::mfma(aop, bop, oacc[db]);
-                }
+            for (int j = 0; j < VPM; j += 2) {
+                const int vi = i * VPM + j, skb = vi / 16, r = vi % 16;
+                mt = fmaxf(mt, fmaxf(s_next[skb][r], s_next[skb][r + 1]));
             }
+            asm volatile("" : "+v"(mt));  // keep the max chain in this phase
+            __builtin_amdgcn_sched_barrier(0);
         }
+        return mt;
+    };
 
-        if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+    // Software pipeline over key tiles.  K is staged one tile ahead of V: iteration t reads
+    // K_{t+1} and V_t from LDS while the loads of K_{t+2} and V_{t+1} fill the buffers that
+    // iteration t-1 finished reading, so one barrier per tile suffices.
+    const int n_tiles = kr.n_tiles;
+    f32x16 s_cur[KB], s_nxt[KB];
+    unsigned pk[KB][8];
+    float mc = 0.f;
+    if (n_tiles > 0) {
+        load_k(0, 0);
+        load_v(0, 0);
+        load_k(1, 1);
+        wait_loads();
         __syncthreads();
+        // scores of tile 0 (no probabilities to overlap yet: phase 1 runs on zeros)
+        float dummy_sum = 0.f;
+        f32x16 zero[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zero[kb][r] = 0.f;
+        phase1(0, s_cur, zero, 0.f, pk, dummy_sum);
+        mc = update_max(mask_max(0, s_cur, kr.n_full > 0));
+        __syncthreads();  // every wave has read K_0 before K_2 overwrites it
+    }
+    int t = 0;
+    for (; t + 1 < n_tiles; ++t) {
+        load_k(t + 2, t & 1);  // rows past N (or a tile past the end) read as zero
+        load_v(t + 1, (t + 1) & 1);
+        float psum = 0.f;
+        phase1((t + 1) & 1, s_nxt, s_cur, mc, pk, psum);
+        l_part += psum;
+        float mt = phase2(t & 1, pk, s_nxt);
+        if (t + 1 >= kr.n_full) mt = mask_max(t + 1, s_nxt);  // diagonal band / ragged tail
+        mc = update_max(mt);
+        wait_loads();
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
+    }
+    if (t < n_tiles) {  // last tile: no scores to prefetch
+        float psum = 0.f;
+        probs(s_cur, mc, pk, psum);
+        l_part += psum;
+        phase2(t & 1, pk, s_nxt);
     }
 
     // ---- A8: epilogue -- normalise once, write O and the logsumexp
