@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 #include "fa_tiles.h"
 
@@ -249,56 +251,121 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
     const int tr_dcol = 16 * (tr_j & 1) + 8 * tr_g + 4 * (tr_j >> 1);
     const int v_rd = (hh * 16 + tr_e) * VP + tr_dcol * 2;
 
-    // The loop body is written as two straight-line phases whose MFMAs are interleaved with
-    // the VALU work of the softmax (the MFMA pipe runs while the wave issues VALU instructions):
-    //   phase 1: S_{t+1} = K_{t+1} Q^T (MFMA)   ||  p = exp2(fma(s, c, -m c)) of tile t, row sums, rounding
-    //   phase 2: O^T += V_t^T P_t^T    (MFMA)   ||  mask and row max of tile t+1
-    // followed, only when some row's running max grew, by the rescale of O.  The order inside
-    // a phase is fixed with scheduling barriers: MFMA i, then its share of VALU work, with the
-    // LDS operands of MFMA i+2 read ahead.
-    constexpr int NM = KS * KB;                 // MFMAs per phase
-    constexpr int PAIRS = KB * 8;               // probability pairs per lane per tile
-    constexpr int PPM = PAIRS / NM;             // pairs per MFMA in phase 1
-    static_assert(PPM * NM == PAIRS, "phase 1 must split evenly");
-    static_assert(NM == KB * 2 * DB, "phase 2 has as many MFMAs as phase 1");
+    // The loop body is one straight-line sequence of 2 NM MFMAs whose issue is interleaved
+    // with the VALU work of the softmax (the MFMA pipe runs while the wave issues VALU work):
+    //   MFMA j <  NM: S_{t+1} += K_{t+1} Q^T      ||  p = exp2(fma(s, c, -m c)) of tile t, in place
+    //   MFMA j >= NM: O^T += V_t^T P_t^T          ||  rounding of p to T and row sums of tile t,
+    //                                                  in-lane row max of tile t+1
+    // followed, only when some row's running max grew, by the rescale of O.  Scheduling
+    // barriers fix the order: MFMA j, then its share of VALU work; the LDS operand of MFMA
+    // j + RA is read while MFMA j issues.
+    constexpr int NM = KS * KB;                 // MFMAs per half step
+    constexpr int VALS = KB * 16;               // score values per lane per tile
+    constexpr int VPM = VALS / NM;              // values handled per MFMA in each half
+    constexpr int NG = 2 * KB;                  // key octets per tile
+    constexpr int CPM = 4 / DB;                 // P dwords rounded per value MFMA
+    constexpr int RA = 3;                       // operand read-ahead, in MFMAs
+    static_assert(VPM * NM == VALS && VPM % 2 == 0, "each half must split evenly");
+    static_assert(NM == KB * 2 * DB && CPM * DB == 4, "value MFMAs: key block x octet x column block");
 
-    // one pair of probabilities: exp2 of the scaled, max-shifted scores, summed and rounded to T
-    auto prob_pair = [&](const f32x16 (&s_cur)[KB], int pi, float mc, unsigned (&pk)[KB][8], float &psum) {
-        const int pkb = pi / 8, pr = (pi % 8) * 2;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[pkb][pr], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[pkb][pr + 1], c, -mc));
-        psum += p0 + p1;
-        pk[pkb][pr / 2] = Elem<T>::pack2(p0, p1);
+    // LDS operand of MFMA j: a K fragment (j < NM) or two transposing V reads (j >= NM).
+    // Value MFMA i = j - NM: key block kb = i / (2 DB), key octet tt = (i / DB) % 2, column block i % DB.
+    auto read_op = [&](int j, const lds_u8 *kp, const lds_u8 *vp) {
+        if (j < NM) return *(const lds_u32x4 *)(kp + (j % KB) * 32 * KP + (j / KB) * 32);
+        const int i = j - NM, kb = i / (2 * DB), tt = (i / DB) % 2, db = i % DB;
+        const int off = (kb * 32 + tt * 8) * VP + db * 64;  // rows k0.., columns of block db
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + off));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + off + 4 * VP));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        return v;
+    };
+    // dword w of key octet g of P: keys 8 (g % 2) + 2 w, +1 of key block g / 2, rounded to T
+    auto cvt = [&](const f32x16 (&pr)[KB], int g, int w) {
+        const int kb = g / 2, r = 8 * (g % 2) + 2 * w;
+        return Elem<T>::pack2(pr[kb][r], pr[kb][r + 1]);
     };
 
-    // ---- A4 (+A6 of the previous tile): scores of the tile in `kbuf`, interleaved with the
-    // probabilities of `s_cur` given the row max scaled by c (mc)
-    auto phase1 = [&](int kbuf, f32x16 (&s_next)[KB], const f32x16 (&s_cur)[KB], float mc,
-                      unsigned (&pk)[KB][8], float &psum) {
-        const lds_u8 *src = smem + kbuf * K_TILE + k_rd;
-        auto rd = [&](int i) { return *(const lds_u32x4 *)(src + (i % KB) * 32 * KP + (i / KB) * 32); };
+    // One step.  QK: also compute the scores s_next of the next tile (from kbuf) and the
+    // probabilities of s_cur (overwritten in place); otherwise s_cur already holds them.
+    // Returns the in-lane max of s_next (unmasked); adds this tile's row sum to psum.
+    auto step = [&](auto qk_tag, int kbuf, int vbuf, f32x16 (&s_next)[KB], f32x16 (&s_cur)[KB], float mc,
+                    float &psum) {
+        constexpr bool QK = decltype(qk_tag)::value;
+        constexpr int J0 = QK ? 0 : NM;  // first MFMA of the sequence
+        const lds_u8 *kp = smem + kbuf * K_TILE + k_rd;
+        const lds_u8 *vp = smem + 2 * K_TILE + vbuf * V_TILE + v_rd;
+        if constexpr (QK) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.f;
-        u32x4 a[3];
-        a[0] = rd(0);
-        a[1] = rd(1);
+                for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.f;
+        }
+        u32x4 a[RA + 1];
 #pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            if (i + 2 < NM) a[(i + 2) % 3] = rd(i + 2);
-            s_next[i % KB] = Elem<T>::mfma(a[i % 3], qreg[i / KB], s_next[i % KB]);
+        for (int j = J0; j < J0 + RA; ++j) a[j % (RA + 1)] = read_op(j, kp, vp);
+        float mt = -INFINITY;
+        u32x4 bop[2];
 #pragma unroll
-            for (int j = 0; j < PPM; ++j) prob_pair(s_cur, i * PPM + j, mc, pk, psum);
-            asm volatile("" : "+v"(psum));  // keep the row-sum chain in this phase
+        for (int j = J0; j < 2 * NM; ++j) {
+            if (j + RA < 2 * NM) a[(j + RA) % (RA + 1)] = read_op(j + RA, kp, vp);
+            if (j < NM) {
+                s_next[j % KB] = Elem<T>::mfma(a[j % (RA + 1)], qreg[j / KB], s_next[j % KB]);
+#pragma unroll
+                for (int e = 0; e < VPM; ++e) {
+                    const int v = j * VPM + e;
+                    s_cur[v / 16][v % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[v / 16][v % 16], c, -mc));
+                }
+                if (j == NM - 1) {  // P octet 0 is needed by the first value MFMA
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) bop[0][w] = cvt(s_cur, 0, w);
+                }
+            } else {
+                const int i = j - NM, g = i / DB;
+                if (!QK && i == 0) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) bop[0][w] = cvt(s_cur, 0, w);
+                }
+                oacc[i % DB] = Elem<T>::mfma(a[j % (RA + 1)], bop[g % 2], oacc[i % DB]);
+                if (g + 1 < NG) {
+#pragma unroll
+                    for (int w = (i % DB) * CPM; w < (i % DB + 1) * CPM; ++w) bop[(g + 1) % 2][w] = cvt(s_cur, g + 1, w);
+                }
+#pragma unroll
+                for (int e = 0; e < VPM; ++e) {
+                    const int v = i * VPM + e;
+                    psum += s_cur[v / 16][v % 16];
+                }
+                if constexpr (QK) {
+#pragma unroll
+                    for (int e = 0; e < VPM; e += 2) {
+                        const int v = i * VPM + e;
+                        mt = fmaxf(mt, fmaxf(s_next[v / 16][v % 16], s_next[v / 16][v % 16 + 1]));
+                    }
+                }
+                asm volatile("" : "+v"(mt), "+v"(psum));  // keep both chains in place
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
+        return mt;
     };
 
     // probabilities of the last tile, with no next tile to overlap
-    auto probs = [&](const f32x16 (&s_cur)[KB], float mc, unsigned (&pk)[KB][8], float &psum) {
+    auto probs = [&](f32x16 (&s_cur)[KB], float mc) {
 #pragma unroll
-        for (int pi = 0; pi < PAIRS; ++pi) prob_pair(s_cur, pi, mc, pk, psum);
+        for (int v = 0; v < VALS; ++v)
+            s_cur[v / 16][v % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[v / 16][v % 16], c, -mc));
+    };
+
+    // scores of one tile only (the first one)
+    auto scores = [&](int kbuf, f32x16 (&s)[KB]) {
+        const lds_u8 *kp = smem + kbuf * K_TILE + k_rd;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NM; ++j) s[j % KB] = Elem<T>::mfma(read_op(j, kp, kp), qreg[j / KB], s[j % KB]);
     };
 
     // ---- A5: visibility of key `key` to this lane's row (diagonal band / ragged last tile)
@@ -339,48 +406,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         return (m_run == -INFINITY ? 0.f : m_run) * c;  // no visible key yet: keep exp2 finite
     };
 
-    // ---- A7: O^T += V^T P^T (P is the B operand straight from registers), interleaved with
-    // the mask (MASK) and in-lane row max of the next tile's scores s_next (first key n0)
-    auto phase2 = [&](int vbuf, const unsigned (&pk)[KB][8], const f32x16 (&s_next)[KB]) {
-        const lds_u8 *src = smem + 2 * K_TILE + vbuf * V_TILE + v_rd;
-        // MFMA i: key block kb = i / (2*DB), key octet tt = (i / DB) % 2, column block db = i % DB
-        auto rd = [&](int i) {
-            const int kb = i / (2 * DB), tt = (i / DB) % 2, db = i % DB;
-            const int off = (kb * 32 + tt * 8) * VP + db * 64;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(src + off));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(src + off + 4 * VP));
-            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-            const u32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
-            return v;
-        };
-        constexpr int VPM = KB * 16 / NM;  // score values of s_next handled per MFMA
-        float mt = -INFINITY;
-        u32x4 a[3];
-        a[0] = rd(0);
-        a[1] = rd(1);
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-            if (i + 2 < NM) a[(i + 2) % 3] = rd(i + 2);
-            const int kb = i / (2 * DB), tt = (i / DB) % 2;
-            const u32x4 bop = {pk[kb][4 * tt], pk[kb][4 * tt + 1], pk[kb][4 * tt + 2], pk[kb][4 * tt + 3]};
-            oacc[i % DB] = Elem<T>::mfma(a[i % 3], bop, oacc[i % DB]);
-#pragma unroll
-            for (int j = 0; j < VPM; j += 2) {
-                const int vi = i * VPM + j, skb = vi / 16, r = vi % 16;
-                mt = fmaxf(mt, fmaxf(s_next[skb][r], s_next[skb][r + 1]));
-            }
-            asm volatile("" : "+v"(mt));  // keep the max chain in this phase
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        return mt;
-    };
-
     // Software pipeline over key tiles.  K is staged one tile ahead of V: iteration t reads
     // K_{t+1} and V_t from LDS while the loads of K_{t+2} and V_{t+1} fill the buffers that
     // iteration t-1 finished reading, so one barrier per tile suffices.
     const int n_tiles = kr.n_tiles;
     f32x16 s_cur[KB], s_nxt[KB];
-    unsigned pk[KB][8];
     float mc = 0.f;
     if (n_tiles > 0) {
         load_k(0, 0);
@@ -388,14 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         load_k(1, 1);
         wait_loads();
         __syncthreads();
-        // scores of tile 0 (no probabilities to overlap yet: phase 1 runs on zeros)
-        float dummy_sum = 0.f;
-        f32x16 zero[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) zero[kb][r] = 0.f;
-        phase1(0, s_cur, zero, 0.f, pk, dummy_sum);
+        scores(0, s_cur);
         mc = update_max(mask_max(0, s_cur, kr.n_full > 0));
         __syncthreads();  // every wave has read K_0 before K_2 overwrites it
     }
@@ -404,9 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         load_k(t + 2, t & 1);  // rows past N (or a tile past the end) read as zero
         load_v(t + 1, (t + 1) & 1);
         float psum = 0.f;
-        phase1((t + 1) & 1, s_nxt, s_cur, mc, pk, psum);
+        float mt = step(std::true_type{}, (t + 1) & 1, t & 1, s_nxt, s_cur, mc, psum);
         l_part += psum;
-        float mt = phase2(t & 1, pk, s_nxt);
         if (t + 1 >= kr.n_full) mt = mask_max(t + 1, s_nxt);  // diagonal band / ragged tail
         mc = update_max(mt);
         wait_loads();
@@ -415,10 +437,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
     }
     if (t < n_tiles) {  // last tile: no scores to prefetch
+        probs(s_cur, mc);
         float psum = 0.f;
-        probs(s_cur, mc, pk, psum);
+        step(std::false_type{}, 0, t & 1, s_nxt, s_cur, mc, psum);
         l_part += psum;
-        phase2(t & 1, pk, s_nxt);
     }
 
     // ---- A8: epilogue -- normalise once, write O and the logsumexp
