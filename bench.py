@@ -184,7 +184,7 @@ def main():
         tflops = flops * args.steps / wall / 1e12
         avg_ms = sum(durs) / len(durs)
         achieved = flops / (avg_ms * 1e-3) / 1e12
-        bm, bn = fa.fa_tile_shape(w.D)
+        bm, bn = fa.fa_tile_shape(w.B, w.Hq, w.M, w.D)
         f_, m_, _ = fa.fa_tile_counts(w.M, w.N, bm, bn, w.causal)
         issued = 4 * bm * bn * w.D * (f_ + m_) * w.B * w.Hq
         line = {

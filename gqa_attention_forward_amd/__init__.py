@@ -7,7 +7,7 @@ fallback: if ``libfa.so`` is missing or cannot be loaded, every call raises.
 Functions with the C ABI's names take raw device pointers and sizes:
 
     fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream)
-    fa_strerror(code), fa_tile_shape(D), fa_tile_counts(...), fa_schedule(...)
+    fa_strerror(code), fa_tile_shape(B, Hq, M, D), fa_tile_counts(...), fa_schedule(...)
 
 and ``attention_forward(q, k, v, causal, scale)`` is the torch-tensor convenience wrapper
 (torch is used only for device memory and the current stream).
@@ -47,7 +47,7 @@ def _load():
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     ip, llp = ctypes.POINTER(ci), ctypes.POINTER(cll)
-    lib.fa_tile_shape.argtypes = [ci, ip, ip]
+    lib.fa_tile_shape.argtypes = [ci, ci, ci, ci, ip, ip]
     lib.fa_tile_shape.restype = ci
     lib.fa_tile_counts.argtypes = [ci, ci, ci, ci, ci, llp, llp, llp]
     lib.fa_tile_counts.restype = ci
@@ -73,9 +73,10 @@ def fa_strerror(code: int) -> str:
     return _load().fa_strerror(int(code)).decode()
 
 
-def fa_tile_shape(D: int):
+def fa_tile_shape(B: int, Hq: int, M: int, D: int):
+    """(BM, BN): query-tile and key-tile heights fa_fwd uses for this problem."""
     bm, bn = ctypes.c_int(), ctypes.c_int()
-    rc = _load().fa_tile_shape(D, ctypes.byref(bm), ctypes.byref(bn))
+    rc = _load().fa_tile_shape(B, Hq, M, D, ctypes.byref(bm), ctypes.byref(bn))
     if rc != FA_OK:
         raise FaError(rc, "fa_tile_shape")
     return bm.value, bn.value

@@ -51,10 +51,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kBN = 64;       // keys per tile
-constexpr int kWaves = 4;     // 32 query rows per wave
-constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;  // keys per tile; a workgroup of W waves owns 32 W query rows
 
 // ---------------------------------------------------------------- element types
 
@@ -131,9 +128,14 @@ struct Params {
 
 // --------------------------------------------------------------------- kernel
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
+// W waves per workgroup (BM = 32 W query rows).  W = 4: two workgroups share a CU, K and V
+// tiles double-buffered.  W = 8: one workgroup per CU (still two waves per SIMD), tiles
+// triple-buffered so that each load has two tiles of time to land.
+template <typename T, int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
 {
+    constexpr int kBM = 32 * W, kWaves = W;
+    constexpr int NBUF = W == 8 ? 3 : 2;
     constexpr int UNITS = D / 8;                       // 16-byte units per row
     constexpr int KS = D / 16;                         // MFMA k-steps over the head dimension
     constexpr int KB = kBN / 32;                       // 32-key blocks per tile
@@ -141,8 +143,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
     constexpr int KP = Lds<D>::K_PITCH, VP = Lds<D>::V_PITCH;
     constexpr int K_TILE = kBN * KP, V_TILE = kBN * VP;
 
-    // [K buf 0 | K buf 1 | V buf 0 | V buf 1]
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * K_TILE + 2 * V_TILE];
+    // [K buf 0 .. NBUF-1 | V buf 0 .. NBUF-1 | 1 KiB sink for padding loads]
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NBUF * (K_TILE + V_TILE) + 1024];
     lds_u8 *smem = (lds_u8 *)smem_raw;
 
     const int tid = threadIdx.x;
@@ -178,14 +180,19 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
     // ---- A3: K and V tiles go from HBM straight into LDS: buffer loads whose destination is
     // LDS, 16 bytes per lane, lane i of one instruction filling bytes [16 i, 16 i + 16) of a
     // 1 KiB block.  Instruction j of a tile fills block j of that tile's LDS buffer; the wave
-    // issues j = wave, wave + 4, ...  Each tile gets its own buffer resource whose size ends at
+    // issues j = wave, wave + W, ...  Each tile gets its own buffer resource whose size ends at
     // N, so key rows past N -- and the lanes that land on pad units, given an offset past any
-    // size -- read as zero without touching memory.
+    // size -- read as zero without touching memory.  Every wave issues the same number of
+    // loads per tile (a wave short of blocks loads nothing into a sink block), so that one
+    // constant wait count covers every wave.
     constexpr int K_INSTR = K_TILE / 1024, V_INSTR = V_TILE / 1024;
     static_assert(K_INSTR * 1024 == K_TILE && V_INSTR * 1024 == V_TILE, "tiles are whole 1 KiB blocks");
     constexpr int KI = (K_INSTR + kWaves - 1) / kWaves, VI = (V_INSTR + kWaves - 1) / kWaves;
+    constexpr int LOADS_PER_TILE = KI + VI;  // per wave
+    static_assert(LOADS_PER_TILE < 16, "wait count encoding");
     constexpr unsigned kPad = 0x7fffff00u;  // an offset past the end of every tile resource
     constexpr int TILE_GBYTES = kBN * D * (int)sizeof(T);
+    lds_u8 *const sink = smem + NBUF * (K_TILE + V_TILE);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const long long kv_bytes = (long long)N * D * (long long)sizeof(T);
     unsigned k_src[KI], v_src[VI];
@@ -194,13 +201,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         const int u = (wave_u + kWaves * i) * 64 + lane;  // 16-byte unit of the K tile this lane fills
         const int slot = u / (KP / 16), unit = u % (KP / 16);
         const int key = (slot & ~31) | pi32(slot & 31);    // slot order pi inside each 32-key block
-        k_src[i] = unit < UNITS ? (unsigned)(key * D * (int)sizeof(T) + unit * 16) : kPad;
+        k_src[i] = unit < UNITS && u < K_INSTR * 64 ? (unsigned)(key * D * (int)sizeof(T) + unit * 16) : kPad;
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
         const int u = (wave_u + kWaves * i) * 64 + lane;
         const int row = u / (VP / 16), unit = u % (VP / 16);
-        v_src[i] = unit < UNITS ? (unsigned)(row * D * (int)sizeof(T) + unit * 16) : kPad;
+        v_src[i] = unit < UNITS && u < V_INSTR * 64 ? (unsigned)(row * D * (int)sizeof(T) + unit * 16) : kPad;
     }
     auto tile_rsrc = [&](const T *base, int t) {
         const long long off = (long long)t * TILE_GBYTES;
@@ -215,22 +222,26 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
             const int j = wave_u + kWaves * i;
-            if (K_INSTR % kWaves == 0 || j < K_INSTR)
-                lds_load16(rs, (lds_void *)(dst + j * 1024), k_src[i]);
+            lds_load16(rs, (lds_void *)(K_INSTR % kWaves == 0 || j < K_INSTR ? dst + j * 1024 : sink), k_src[i]);
         }
     };
     auto load_v = [&](int t, int buf) {
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, t);
-        lds_u8 *dst = smem + 2 * K_TILE + buf * V_TILE;
+        lds_u8 *dst = smem + NBUF * K_TILE + buf * V_TILE;
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
             const int j = wave_u + kWaves * i;
-            if (V_INSTR % kWaves == 0 || j < V_INSTR)
-                lds_load16(rs, (lds_void *)(dst + j * 1024), v_src[i]);
+            lds_load16(rs, (lds_void *)(V_INSTR % kWaves == 0 || j < V_INSTR ? dst + j * 1024 : sink), v_src[i]);
         }
     };
-    // this wave's loads into LDS have landed (vmcnt(0)); a barrier then publishes them
-    auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+    // this wave's loads into LDS, except the newest `keep` tiles' worth, have landed; a barrier
+    // then publishes them (s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maximum)
+    auto wait_loads = [&](auto keep_tag) {
+        constexpr int n = decltype(keep_tag)::value * LOADS_PER_TILE;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+    };
+    using Keep0 = std::integral_constant<int, 0>;
+    using Keep1 = std::integral_constant<int, 1>;
 
     // ---- online-softmax state (A6) and output accumulator
     f32x16 oacc[DB];
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         constexpr bool QK = decltype(qk_tag)::value;
         constexpr int J0 = QK ? 0 : NM;  // first MFMA of the sequence
         const lds_u8 *kp = smem + kbuf * K_TILE + k_rd;
-        const lds_u8 *vp = smem + 2 * K_TILE + vbuf * V_TILE + v_rd;
+        const lds_u8 *vp = smem + NBUF * K_TILE + vbuf * V_TILE + v_rd;
         if constexpr (QK) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -409,6 +420,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
     // Software pipeline over key tiles.  K is staged one tile ahead of V: iteration t reads
     // K_{t+1} and V_t from LDS while the loads of K_{t+2} and V_{t+1} fill the buffers that
     // iteration t-1 finished reading, so one barrier per tile suffices.
+    // Software pipeline over key tiles.  Iteration t reads K_{t+1} (scores of the next tile)
+    // and V_t from LDS, and issues the loads of K_{t+NBUF} and V_{t+NBUF-1} into the buffers
+    // that iteration t-1 finished reading; one barrier per tile publishes the loads issued
+    // NBUF-2 iterations earlier.
     const int n_tiles = kr.n_tiles;
     f32x16 s_cur[KB], s_nxt[KB];
     float mc = 0.f;
@@ -416,30 +431,43 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
         load_k(0, 0);
         load_v(0, 0);
         load_k(1, 1);
-        wait_loads();
+        if constexpr (NBUF == 3) {
+            load_k(2, 2);
+            load_v(1, 1);
+            wait_loads(Keep1{});
+        } else {
+            wait_loads(Keep0{});
+        }
         __syncthreads();
         scores(0, s_cur);
         mc = update_max(mask_max(0, s_cur, kr.n_full > 0));
-        __syncthreads();  // every wave has read K_0 before K_2 overwrites it
+        __syncthreads();  // every wave has read K_0 before its buffer is refilled
     }
     int t = 0;
+    int kb_next = 1 % NBUF, vb_cur = 0, b_load = 0;  // buffers of K_{t+1}, V_t, and of the loads (t % NBUF)
     for (; t + 1 < n_tiles; ++t) {
-        load_k(t + 2, t & 1);  // rows past N (or a tile past the end) read as zero
-        load_v(t + 1, (t + 1) & 1);
+        load_k(t + NBUF, b_load);  // rows past N (or a tile past the end) read as zero
+        load_v(t + NBUF - 1, (b_load + NBUF - 1) % NBUF);
         float psum = 0.f;
-        float mt = step(std::true_type{}, (t + 1) & 1, t & 1, s_nxt, s_cur, mc, psum);
+        float mt = step(std::true_type{}, kb_next, vb_cur, s_nxt, s_cur, mc, psum);
         l_part += psum;
         if (t + 1 >= kr.n_full) mt = mask_max(t + 1, s_nxt);  // diagonal band / ragged tail
         mc = update_max(mt);
-        wait_loads();
+        if constexpr (NBUF == 3)
+            wait_loads(Keep1{});
+        else
+            wait_loads(Keep0{});
         __syncthreads();
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
+        kb_next = kb_next + 1 == NBUF ? 0 : kb_next + 1;
+        vb_cur = vb_cur + 1 == NBUF ? 0 : vb_cur + 1;
+        b_load = b_load + 1 == NBUF ? 0 : b_load + 1;
     }
     if (t < n_tiles) {  // last tile: no scores to prefetch
         probs(s_cur, mc);
         float psum = 0.f;
-        step(std::false_type{}, 0, t & 1, s_nxt, s_cur, mc, psum);
+        step(std::false_type{}, 0, vb_cur, s_nxt, s_cur, mc, psum);
         l_part += psum;
     }
 
@@ -474,29 +502,38 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p)
 
 // ------------------------------------------------------------------ host side
 
-static int tile_shape(int D, int *BM, int *BN)
+// Launch plan: 8-wave workgroups (256 query rows) when they alone fill every CU once,
+// 4-wave workgroups otherwise (small grids need the larger workgroup count).
+static int waves_for(int B, int Hq, int M)
+{
+    const long long wg8 = (long long)B * Hq * ((M + 255) / 256);
+    return wg8 >= 256 ? 8 : 4;
+}
+
+static int tile_shape(int B, int Hq, int M, int D, int *BM, int *BN)
 {
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-    *BM = kBM;
+    *BM = 32 * waves_for(B, Hq, M);
     *BN = kBN;
     return FA_OK;
 }
 
-template <typename T, int D>
-static hipError_t launch_d(const Params &p, bool causal, hipStream_t stream)
+template <typename T, int D, int W>
+static hipError_t launch_w(const Params &p, bool causal, hipStream_t stream)
 {
-    dim3 grid((unsigned)p.total), block(kThreads);
+    dim3 grid((unsigned)p.total), block(64 * W);
     if (causal)
-        hipLaunchKernelGGL((fa_fwd_kernel<T, D, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, true, W>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((fa_fwd_kernel<T, D, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, W>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_t(const Params &p, int D, bool causal, hipStream_t stream)
+static hipError_t launch_t(const Params &p, int D, int W, bool causal, hipStream_t stream)
 {
-    return D == 128 ? launch_d<T, 128>(p, causal, stream) : launch_d<T, 64>(p, causal, stream);
+    if (D == 128) return W == 8 ? launch_w<T, 128, 8>(p, causal, stream) : launch_w<T, 128, 4>(p, causal, stream);
+    return W == 8 ? launch_w<T, 64, 8>(p, causal, stream) : launch_w<T, 64, 4>(p, causal, stream);
 }
 
 }  // namespace fa
@@ -514,10 +551,10 @@ const char *fa_strerror(int code)
     }
 }
 
-int fa_tile_shape(int D, int *BM, int *BN)
+int fa_tile_shape(int B, int Hq, int M, int D, int *BM, int *BN)
 {
-    if (!BM || !BN) return FA_ERR_INVALID_ARG;
-    return fa::tile_shape(D, BM, BN);
+    if (!BM || !BN || B <= 0 || Hq <= 0 || M <= 0) return FA_ERR_INVALID_ARG;
+    return fa::tile_shape(B, Hq, M, D, BM, BN);
 }
 
 int fa_tile_counts(int M, int N, int BM, int BN, int causal, long long *full, long long *masked, long long *skipped)
@@ -541,7 +578,7 @@ int fa_schedule(int B, int Hq, int Hkv, int M, int D, int causal, long long wg, 
 {
     int BM, BN;
     if (!b || !h || !q_tile || B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-    if (fa::tile_shape(D, &BM, &BN) != FA_OK) return FA_ERR_INVALID_ARG;
+    if (fa::tile_shape(B, Hq, M, D, &BM, &BN) != FA_OK) return FA_ERR_INVALID_ARG;
     const int n_qt = (M + BM - 1) / BM;
     const long long total = (long long)B * Hq * n_qt;
     if (wg < 0 || wg >= total) return FA_ERR_INVALID_ARG;
@@ -564,7 +601,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     const double nq = (double)B * Hq * M * D, nk = (double)B * Hkv * N * D;
     if (nq > 9.0e18 || nk > 9.0e18) return FA_ERR_INVALID_ARG;
     int BM, BN;
-    if (fa::tile_shape(D, &BM, &BN) != FA_OK) return FA_ERR_UNSUPPORTED;
+    if (fa::tile_shape(B, Hq, M, D, &BM, &BN) != FA_OK) return FA_ERR_UNSUPPORTED;
+    // K and V of one (b, kv head) are addressed with 32-bit buffer offsets
+    if ((long long)N * D * 2 > 0x7fff0000LL) return FA_ERR_UNSUPPORTED;
     const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
     if (align & 15u) return FA_ERR_UNSUPPORTED;
 
@@ -585,8 +624,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     p.c = scale * 1.44269504088896340736f;                    // log2(e)
 
     hipStream_t s = (hipStream_t)stream;
-    hipError_t err = dtype == FA_F16 ? fa::launch_t<_Float16>(p, D, causal != 0, s)
-                                     : fa::launch_t<__bf16>(p, D, causal != 0, s);
+    const int W = BM / 32;
+    hipError_t err = dtype == FA_F16 ? fa::launch_t<_Float16>(p, D, W, causal != 0, s)
+                                     : fa::launch_t<__bf16>(p, D, W, causal != 0, s);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -43,7 +43,8 @@ enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, Hq % Hkv != 0, scale not finite or <= 0,
                                 unknown dtype, sizes whose element counts overflow int64 */
-    FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, or a pointer not 16-byte aligned */
+    FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, a pointer not 16-byte aligned, one KV head's K (or V)
+                                larger than 2 GiB, or a grid beyond 2^31 - 1 workgroups */
     FA_ERR_LAUNCH = -3       /* the kernel launch reported an error (hipGetLastError) */
 };
 
@@ -83,8 +84,11 @@ const char *fa_strerror(int code);
  * fa_fwd uses, so that tests can check the tile classification against the pages' worked
  * counts and benchmarks can count the work actually issued.
  *
- * fa_tile_shape: the query-tile and key-tile heights fa_fwd uses for head dimension D.
- *   Returns FA_OK, or FA_ERR_UNSUPPORTED for an unsupported D.
+ * fa_tile_shape: the query-tile and key-tile heights fa_fwd uses for a problem with B batches,
+ *   Hq query heads, M queries per head and head dimension D (query tiles of 256 rows when the
+ *   grid still fills the GPU, 128 rows otherwise; key tiles of 64 rows).  Returns FA_OK,
+ *   FA_ERR_INVALID_ARG for a null pointer or non-positive size, FA_ERR_UNSUPPORTED for an
+ *   unsupported D.
  *
  * fa_tile_counts: for one (b, h), with query tiles of BM rows and key tiles of BN rows,
  *   counts the key tiles visited without a mask (*full), with a mask (*masked: the
@@ -94,9 +98,10 @@ const char *fa_strerror(int code);
  *   and "改进3-两阶段计算".  Returns FA_OK or FA_ERR_INVALID_ARG.
  *
  * fa_schedule: the (b, h, query-tile) that workgroup `wg` of fa_fwd's grid computes,
- *   for a launch of B * Hq * ceil(M / BM) workgroups.  Returns FA_OK or FA_ERR_INVALID_ARG.
+ *   for a launch of B * Hq * ceil(M / BM) workgroups (BM as fa_tile_shape reports).  Returns
+ *   FA_OK or FA_ERR_INVALID_ARG.
  */
-int fa_tile_shape(int D, int *BM, int *BN);
+int fa_tile_shape(int B, int Hq, int M, int D, int *BM, int *BN);
 int fa_tile_counts(int M, int N, int BM, int BN, int causal, long long *full, long long *masked,
                    long long *skipped);
 int fa_schedule(int B, int Hq, int Hkv, int M, int D, int causal, long long wg, int *b, int *h, int *q_tile);

@@ -53,6 +53,11 @@ SMALL = [
     (3, 2, 1, 1, 1, 128, True, torch.float16),           # one query, one key
     (1, 2, 1, 1, 500, 128, True, torch.float16),         # decode-like: one query row
     (1, 2, 2, 64, 64, 128, False, torch.bfloat16),       # a single half-filled query tile
+    # grids large enough for the 8-wave (256-row) workgroups, ragged in M and N
+    (8, 32, 8, 300, 333, 128, True, torch.bfloat16),
+    (4, 64, 64, 260, 130, 64, False, torch.float16),
+    (2, 128, 16, 513, 700, 128, True, torch.float16),
+    (1, 256, 32, 256, 64, 64, True, torch.bfloat16),      # exactly one key tile per row
 ]
 
 

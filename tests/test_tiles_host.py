@@ -68,10 +68,16 @@ def test_classification_matches_brute_force(M, N, BM, BN, causal):
 
 
 def test_tile_shape():
-    assert fa.fa_tile_shape(128) == (128, 64)
-    assert fa.fa_tile_shape(64) == (128, 64)
+    # 8-wave workgroups (256 rows) once they alone fill the 256 CUs, 4-wave ones below that
+    assert fa.fa_tile_shape(1, 32, 16384, 128) == (256, 64)
+    assert fa.fa_tile_shape(8, 32, 4096, 128) == (256, 64)
+    assert fa.fa_tile_shape(4, 32, 512, 128) == (256, 64)
+    assert fa.fa_tile_shape(2, 16, 1024, 128) == (128, 64)
+    assert fa.fa_tile_shape(1, 2, 128, 64) == (128, 64)
     with pytest.raises(fa.FaError):
-        fa.fa_tile_shape(96)
+        fa.fa_tile_shape(1, 2, 128, 96)
+    with pytest.raises(fa.FaError):
+        fa.fa_tile_shape(0, 2, 128, 64)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,M,causal", [
@@ -79,7 +85,7 @@ def test_tile_shape():
     (2, 5, 5, 129, False), (1, 3, 1, 1, True),
 ])
 def test_schedule_is_a_bijection(B, Hq, Hkv, M, causal):
-    BM, _ = fa.fa_tile_shape(128)
+    BM, _ = fa.fa_tile_shape(B, Hq, M, 128)
     n_qt = (M + BM - 1) // BM
     total = B * Hq * n_qt
     seen = set(fa.fa_schedule(B, Hq, Hkv, M, 128, causal, w) for w in range(total))
@@ -92,7 +98,7 @@ def test_schedule_keeps_kv_groups_on_one_xcd():
     """For the long causal GQA prefill shape, each of the 8 XCDs (wg % 8) serves exactly one
     KV head, and issues its query tiles longest-first."""
     B, Hq, Hkv, M = 1, 32, 8, 16384
-    BM, _ = fa.fa_tile_shape(128)
+    BM, _ = fa.fa_tile_shape(B, Hq, M, 128)
     total = B * Hq * (M // BM)
     per_xcd = {x: [] for x in range(8)}
     for w in range(total):
