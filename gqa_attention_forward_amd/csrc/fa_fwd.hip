@@ -443,28 +443,41 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         mc = update_max(mask_max(0, s_cur, kr.n_full > 0));
         __syncthreads();  // every wave has read K_0 before its buffer is refilled
     }
-    int t = 0;
     int kb_next = 1 % NBUF, vb_cur = 0, b_load = 0;  // buffers of K_{t+1}, V_t, and of the loads (t % NBUF)
-    for (; t + 1 < n_tiles; ++t) {
+    auto advance = [&](int &b) { b = b + 1 == NBUF ? 0 : b + 1; };
+    // one full step: probabilities and P V of tile t (scores in cur), scores of tile t+1 into nxt
+    auto body = [&](int t, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
         load_k(t + NBUF, b_load);  // rows past N (or a tile past the end) read as zero
         load_v(t + NBUF - 1, (b_load + NBUF - 1) % NBUF);
         float psum = 0.f;
-        float mt = step(std::true_type{}, kb_next, vb_cur, s_nxt, s_cur, mc, psum);
+        float mt = step(std::true_type{}, kb_next, vb_cur, nxt, cur, mc, psum);
         l_part += psum;
-        if (t + 1 >= kr.n_full) mt = mask_max(t + 1, s_nxt);  // diagonal band / ragged tail
+        if (t + 1 >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
         mc = update_max(mt);
         if constexpr (NBUF == 3)
             wait_loads(Keep1{});
         else
             wait_loads(Keep0{});
         __syncthreads();
+        advance(kb_next);
+        advance(vb_cur);
+        advance(b_load);
+    };
+    // Full steps come in pairs with the two score arrays swapping roles (no copies); an odd
+    // count starts with one step and one copy.
+    const int n_steps = n_tiles - 1;
+    int t = 0;
+    if (n_steps > 0 && (n_steps & 1)) {
+        body(0, s_cur, s_nxt);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
-        kb_next = kb_next + 1 == NBUF ? 0 : kb_next + 1;
-        vb_cur = vb_cur + 1 == NBUF ? 0 : vb_cur + 1;
-        b_load = b_load + 1 == NBUF ? 0 : b_load + 1;
+        t = 1;
     }
-    if (t < n_tiles) {  // last tile: no scores to prefetch
+    for (; t < n_steps; t += 2) {
+        body(t, s_cur, s_nxt);
+        body(t + 1, s_nxt, s_cur);
+    }
+    if (n_tiles > 0) {  // last tile: no scores to prefetch
         probs(s_cur, mc);
         float psum = 0.f;
         step(std::false_type{}, 0, vb_cur, s_nxt, s_cur, mc, psum);
