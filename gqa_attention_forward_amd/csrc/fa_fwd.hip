@@ -262,6 +262,44 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
     const int tr_dcol = 16 * (tr_j & 1) + 8 * tr_g + 4 * (tr_j >> 1);
     const int v_rd = (hh * 16 + tr_e) * VP + tr_dcol * 2;
 
+    // ---- A5: visibility of key `key` to this lane's row (diagonal band / ragged last tile)
+    auto visible = [&](int key) { return key < N && (!CAUSAL || key <= causal_lim); };
+
+    // mask (unless `none`) the scores of tile t, then return their in-lane max
+    auto mask_max = [&](int t, f32x16 (&sc)[KB], bool none = false) {
+        const int n0 = t * kBN;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (!none) sc[kb][r] = visible(n0 + kb * 32 + hh * 16 + r) ? sc[kb][r] : -INFINITY;
+                mt = fmaxf(mt, sc[kb][r]);
+            }
+        return mt;
+    };
+
+    // ---- A6: cross-half row max and running-max update.  O and the partial sum are rescaled only
+    // when some row's max grew (alpha = exp2((m_old - m_new) * c) is exactly 1 otherwise);
+    // returns m * c for the exp2 of the tile
+    auto update_max = [&](float mt) {
+        auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mt), __builtin_bit_cast(unsigned, mt),
+                                                   false, false);
+        mt = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
+        const float m_new = fmaxf(m_run, mt);
+        const bool grew = m_new > m_run;
+        if (__any(grew)) {
+            const float alpha = grew ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;  // 0 from -inf
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+        return (m_run == -INFINITY ? 0.f : m_run) * c;  // no visible key yet: keep exp2 finite
+    };
+
     // The loop body is one straight-line sequence of 2 NM MFMAs whose issue is interleaved
     // with the VALU work of the softmax (the MFMA pipe runs while the wave issues VALU work):
     //   MFMA j <  NM: S_{t+1} += K_{t+1} Q^T      ||  p = exp2(fma(s, c, -m c)) of tile t, in place
@@ -276,6 +314,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
     constexpr int NG = 2 * KB;                  // key octets per tile
     constexpr int CPM = 4 / DB;                 // P dwords rounded per value MFMA
     constexpr int RA = 3;                       // operand read-ahead, in MFMAs
+    constexpr int NPRE = 2;                     // score MFMAs issued before the running-max update
     static_assert(VPM * NM == VALS && VPM % 2 == 0, "each half must split evenly");
     static_assert(NM == KB * 2 * DB && CPM * DB == 4, "value MFMAs: key block x octet x column block");
 
@@ -300,9 +339,10 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
     // One step.  QK: also compute the scores s_next of the next tile (from kbuf) and the
     // probabilities of s_cur (overwritten in place); otherwise s_cur already holds them.
     // Returns the in-lane max of s_next (unmasked); adds this tile's row sum to psum.
-    auto step = [&](auto qk_tag, int kbuf, int vbuf, f32x16 (&s_next)[KB], f32x16 (&s_cur)[KB], float mc,
+    auto step = [&](auto qk_tag, int kbuf, int vbuf, f32x16 (&s_next)[KB], f32x16 (&s_cur)[KB], float mt_cur,
                     float &psum) {
         constexpr bool QK = decltype(qk_tag)::value;
+        float mc = 0.f;  // m * c of tile t, set by the running-max update inside the sequence
         constexpr int J0 = QK ? 0 : NM;  // first MFMA of the sequence
         const lds_u8 *kp = smem + kbuf * K_TILE + k_rd;
         const lds_u8 *vp = smem + NBUF * K_TILE + vbuf * V_TILE + v_rd;
@@ -322,10 +362,20 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
             if (j + RA < 2 * NM) a[(j + RA) % (RA + 1)] = read_op(j + RA, kp, vp);
             if (j < NM) {
                 s_next[j % KB] = Elem<T>::mfma(a[j % (RA + 1)], qreg[j / KB], s_next[j % KB]);
+                // the running-max update of tile t (and the rare rescale of O) runs while the
+                // first score MFMAs of tile t+1 execute; the probabilities follow
+                if (j == NPRE - 1) mc = update_max(mt_cur);
+                if (j >= NPRE) {
+                    constexpr int SLOTS = NM - NPRE;
 #pragma unroll
-                for (int e = 0; e < VPM; ++e) {
-                    const int v = j * VPM + e;
-                    s_cur[v / 16][v % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[v / 16][v % 16], c, -mc));
+                    for (int pr = (j - NPRE) * (VALS / 2) / SLOTS; pr < (j - NPRE + 1) * (VALS / 2) / SLOTS; ++pr) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int v = 2 * pr + e;
+                            s_cur[v / 16][v % 16] =
+                                __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[v / 16][v % 16], c, -mc));
+                        }
+                    }
                 }
                 if (j == NM - 1) {  // P octet 0 is needed by the first value MFMA
 #pragma unroll
@@ -379,43 +429,6 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         for (int j = 0; j < NM; ++j) s[j % KB] = Elem<T>::mfma(read_op(j, kp, kp), qreg[j / KB], s[j % KB]);
     };
 
-    // ---- A5: visibility of key `key` to this lane's row (diagonal band / ragged last tile)
-    auto visible = [&](int key) { return key < N && (!CAUSAL || key <= causal_lim); };
-
-    // mask (unless `none`) the scores of tile t, then return their in-lane max
-    auto mask_max = [&](int t, f32x16 (&sc)[KB], bool none = false) {
-        const int n0 = t * kBN;
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (!none) sc[kb][r] = visible(n0 + kb * 32 + hh * 16 + r) ? sc[kb][r] : -INFINITY;
-                mt = fmaxf(mt, sc[kb][r]);
-            }
-        return mt;
-    };
-
-    // ---- A6: cross-half row max and running-max update.  O and the partial sum are rescaled only
-    // when some row's max grew (alpha = exp2((m_old - m_new) * c) is exactly 1 otherwise);
-    // returns m * c for the exp2 of the tile
-    auto update_max = [&](float mt) {
-        auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mt), __builtin_bit_cast(unsigned, mt),
-                                                   false, false);
-        mt = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
-        const float m_new = fmaxf(m_run, mt);
-        const bool grew = m_new > m_run;
-        if (__any(grew)) {
-            const float alpha = grew ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;  // 0 from -inf
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
-        }
-        return (m_run == -INFINITY ? 0.f : m_run) * c;  // no visible key yet: keep exp2 finite
-    };
 
     // Software pipeline over key tiles.  K is staged one tile ahead of V: iteration t reads
     // K_{t+1} and V_t from LDS while the loads of K_{t+2} and V_{t+1} fill the buffers that
@@ -426,7 +439,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
     // NBUF-2 iterations earlier.
     const int n_tiles = kr.n_tiles;
     f32x16 s_cur[KB], s_nxt[KB];
-    float mc = 0.f;
+    float mt_pending = -INFINITY;  // in-lane max of the scores whose running-max update is pending
     if (n_tiles > 0) {
         load_k(0, 0);
         load_v(0, 0);
@@ -440,7 +453,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         }
         __syncthreads();
         scores(0, s_cur);
-        mc = update_max(mask_max(0, s_cur, kr.n_full > 0));
+        mt_pending = mask_max(0, s_cur, kr.n_full > 0);
         __syncthreads();  // every wave has read K_0 before its buffer is refilled
     }
     int kb_next = 1 % NBUF, vb_cur = 0, b_load = 0;  // buffers of K_{t+1}, V_t, and of the loads (t % NBUF)
@@ -450,10 +463,10 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         load_k(t + NBUF, b_load);  // rows past N (or a tile past the end) read as zero
         load_v(t + NBUF - 1, (b_load + NBUF - 1) % NBUF);
         float psum = 0.f;
-        float mt = step(std::true_type{}, kb_next, vb_cur, nxt, cur, mc, psum);
+        float mt = step(std::true_type{}, kb_next, vb_cur, nxt, cur, mt_pending, psum);
         l_part += psum;
         if (t + 1 >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
-        mc = update_max(mt);
+        mt_pending = mt;
         if constexpr (NBUF == 3)
             wait_loads(Keep1{});
         else
@@ -478,9 +491,10 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         body(t + 1, s_nxt, s_cur);
     }
     if (n_tiles > 0) {  // last tile: no scores to prefetch
+        const float mc = update_max(mt_pending);
         probs(s_cur, mc);
         float psum = 0.f;
-        step(std::false_type{}, 0, vb_cur, s_nxt, s_cur, mc, psum);
+        step(std::false_type{}, 0, vb_cur, s_nxt, s_cur, -INFINITY, psum);
         l_part += psum;
     }
 
