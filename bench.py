@@ -50,6 +50,8 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--split-kv", default="auto",
+                    help="'auto' (key-split forward for small grids), 'off', or key tiles per share")
     return ap.parse_args()
 
 
@@ -71,21 +73,35 @@ def read_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def time_gpu(fa, w, q, k, v, steps, warmup):
+def roofline(w, flops, avg_ms, traffic):
+    """The bound that applies to the workload: MFMA when its arithmetic intensity (causal-adjusted
+    flops per compulsory HBM byte) exceeds the machine balance, HBM otherwise (decode-like shapes)."""
+    from gqa_attention_forward_amd import accounting
+
+    nbytes = accounting.workload_bytes(w)
+    if flops / nbytes >= MFMA_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        achieved, peak, bound, unit = flops / (avg_ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS, "mfma", "TFLOP/s"
+    else:
+        achieved, peak, bound, unit = nbytes / (avg_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "hbm", "GB/s"
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel_avg_us": round(avg_ms * 1e3, 3)}
+
+
+def time_gpu(fa, w, q, k, v, steps, warmup, split_kv="auto"):
     import torch
 
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.M), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, split_kv=split_kv)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
-        fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, split_kv=split_kv)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -166,20 +182,29 @@ def main():
 
     import gqa_attention_forward_amd as fa
     from gqa_attention_forward_amd import accounting
-    from gqa_attention_forward_amd.inputs import WORKLOADS, WORKLOAD_ORDER, make_inputs
+    from gqa_attention_forward_amd.inputs import ALL_WORKLOADS as WORKLOADS, make_inputs
 
     if not os.path.exists(fa.LIB_PATH):
         from gqa_attention_forward_amd import build as hip_build
 
         hip_build.build()
 
-    names = WORKLOAD_ORDER if args.all else [args.workload]
+    split_kv = {"auto": "auto", "off": False}.get(args.split_kv)
+    if split_kv is None:
+        split_kv = int(args.split_kv)
+    names = list(WORKLOADS) if args.all else [args.workload]
     result = None
     for name in names:
         w = WORKLOADS[name]
         q, k, v, _ = make_inputs(w, device="cuda")
         torch.cuda.synchronize()
-        wall, durs, o, lse = time_gpu(fa, w, q, k, v, args.steps, args.warmup)
+        wall, durs, o, lse = time_gpu(fa, w, q, k, v, args.steps, args.warmup, split_kv)
+        path = "fa_fwd"
+        if split_kv is not False and w.M <= 16384:
+            tiles, wgs, ws = fa.fa_splitkv_plan(w.B, w.Hq, w.Hkv, w.M, w.N, w.D, w.causal,
+                                                0 if split_kv == "auto" else split_kv)
+            if ws > 0 or split_kv != "auto":
+                path = f"fa_fwd_splitkv ({tiles} key tiles a share, {wgs} workgroups, merge)"
         flops = accounting.workload_flops(w)
         tflops = flops * args.steps / wall / 1e12
         avg_ms = sum(durs) / len(durs)
@@ -188,7 +213,7 @@ def main():
         f_, m_, _ = fa.fa_tile_counts(w.M, w.N, bm, bn, w.causal)
         issued = 4 * bm * bn * w.D * (f_ + m_) * w.B * w.Hq
         line = {
-            "workload": name, "tflops": round(tflops, 2), "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "workload": name, "path": path, "tflops": round(tflops, 2), "kernel_avg_us": round(avg_ms * 1e3, 2),
             "kernel_median_us": round(durs[len(durs) // 2] * 1e3, 2), "kernel_min_us": round(durs[0] * 1e3, 2),
             "pct_mfma_peak": round(100 * achieved / MFMA_PEAK_TFLOPS, 2),
             "issued_mfma_tflops": round(issued / (avg_ms * 1e-3) / 1e12, 2),
@@ -215,10 +240,7 @@ def main():
                            "causal": w.causal, "seed": w.seed, "peaky_k_rows": w.peak_rate,
                            "parallelism": "single GPU"},
                 "pct_of_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 3),
-                "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
-                             "traffic": traffic,
-                             "kernel_avg_us": round(avg_ms * 1e3, 3)},
+                "roofline": roofline(w, flops, avg_ms, traffic),
                 "cpu_baseline": None,
             }
             if not args.no_cpu_baseline:

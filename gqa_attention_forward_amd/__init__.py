@@ -7,10 +7,12 @@ fallback: if ``libfa.so`` is missing or cannot be loaded, every call raises.
 Functions with the C ABI's names take raw device pointers and sizes:
 
     fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream)
+    fa_fwd_splitkv(..., dtype, tiles_per_split, workspace_ptr, workspace_bytes, stream)
+    fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles_per_split)
     fa_strerror(code), fa_tile_shape(B, Hq, M, D), fa_tile_counts(...), fa_schedule(...)
 
-and ``attention_forward(q, k, v, causal, scale)`` is the torch-tensor convenience wrapper
-(torch is used only for device memory and the current stream).
+and ``attention_forward(q, k, v, causal, scale, split_kv)`` is the torch-tensor convenience
+wrapper (torch is used only for device memory, the split workspace and the current stream).
 """
 from __future__ import annotations
 
@@ -53,6 +55,11 @@ def _load():
     lib.fa_tile_counts.restype = ci
     lib.fa_schedule.argtypes = [ci, ci, ci, ci, ci, ci, cll, ip, ip, ip]
     lib.fa_schedule.restype = ci
+    sz = ctypes.c_size_t
+    lib.fa_splitkv_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ip, llp, ctypes.POINTER(sz)]
+    lib.fa_splitkv_plan.restype = ci
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, ci, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = ci
     _lib = lib
     return lib
 
@@ -67,6 +74,23 @@ def library():
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream) -> int:
     """Raw C ABI call: pointers are integers (device addresses), stream an int or None."""
     return _load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, M, N, D, float(scale), int(causal), int(dtype), stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, causal, dtype, tiles_per_split, workspace,
+                   workspace_bytes, stream) -> int:
+    """Raw C ABI call of the key-split forward (pointers as integers)."""
+    return _load().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, M, N, D, float(scale), int(causal), int(dtype),
+                                  int(tiles_per_split), workspace, int(workspace_bytes), stream)
+
+
+def fa_splitkv_plan(B: int, Hq: int, Hkv: int, M: int, N: int, D: int, causal: bool, tiles_per_split: int = 0):
+    """(tiles_used, workgroups, workspace_bytes) of the key-split forward for this problem."""
+    t, wg, ws = ctypes.c_int(), ctypes.c_longlong(), ctypes.c_size_t()
+    rc = _load().fa_splitkv_plan(B, Hq, Hkv, M, N, D, int(bool(causal)), int(tiles_per_split), ctypes.byref(t),
+                                 ctypes.byref(wg), ctypes.byref(ws))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_splitkv_plan")
+    return t.value, wg.value, ws.value
 
 
 def fa_strerror(code: int) -> str:
@@ -113,10 +137,16 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
 
 
-def attention_forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None):
+def attention_forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None,
+                      split_kv="auto"):
     """O, lse = softmax(mask(q k^T * scale)) v for contiguous device tensors
     q [B,Hq,M,D], k/v [B,Hkv,N,D] (fp16 or bf16).  Returns (o [B,Hq,M,D], lse [B,Hq,M] fp32).
-    The kernel is enqueued on `stream` (default: torch's current stream) and not waited for."""
+
+    split_kv: "auto" runs the key-split forward when its plan splits some query tile (small
+    grids) and fa_fwd otherwise; False always runs fa_fwd; an int > 0 runs the key-split forward
+    with at most that many key tiles per share.  The split workspace comes from torch's caching
+    allocator.  Kernels are enqueued on `stream` (default: torch's current stream) and not
+    waited for."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -140,6 +170,22 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
         lse = torch.empty((B, Hq, M), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    if split_kv is not False:
+        tiles = 0 if split_kv == "auto" else int(split_kv)
+        if tiles < 0:
+            raise ValueError("split_kv must be 'auto', False or a positive tile count")
+        M_ok = M <= 128 * 128  # the split plan describes at most 128 query tiles per head
+        if M_ok and D in (64, 128):
+            _, _, ws_bytes = fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles)
+            if ws_bytes > 0 or split_kv != "auto":
+                ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+                rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                                    Hkv, M, N, D, scale, causal, _dtype_code(q), tiles, ws.data_ptr(), ws_bytes, stream)
+                if rc != FA_OK:
+                    raise FaError(rc, "fa_fwd_splitkv")
+                return out, lse
+        elif split_kv != "auto":
+            raise ValueError("the key-split forward needs D in (64, 128) and M <= 16384")
     rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, M, N, D,
                 scale, causal, _dtype_code(q), stream)
     if rc != FA_OK:
@@ -147,5 +193,5 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
-__all__ = ["fa_fwd", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_splitkv_plan", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]

@@ -43,6 +43,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -126,13 +127,31 @@ struct Params {
     float c;            // scale * log2(e)
 };
 
+// Key-split mode.  The key tiles a query tile visits are divided over n_split workgroups (an
+// even share each); each writes the normalised output and natural-log lse of its share to the
+// workspace, and a merge kernel combines them.  A query tile with one share writes O and lse
+// directly.  Query tiles are taken in rank order (longest first when causal), so the shares
+// per tile never grow with the rank and the split tiles are the ranks [0, n_split_ranks).
+constexpr int kMaxSplitQt = 128;  // query tiles per (b, h) the split plan can describe
+struct SplitParams : Params {
+    int wg_per_head;    // workgroups per (b, h): prefix[n_qt]
+    int slots;          // partial slots per (b, h): prefix[n_split_ranks]
+    int n_split_ranks;
+    int causal;
+    int slot_rows;      // rows a slot holds: min(BM, M)
+    float *ws_lse;      // [B*Hq][slots][slot_rows]
+    float *ws_o;        // [B*Hq][slots][slot_rows][D]
+    int prefix[kMaxSplitQt + 1];  // workgroups of the query-tile ranks below r
+};
+
+
 // --------------------------------------------------------------------- kernel
 
 // W waves per workgroup (BM = 32 W query rows).  W = 4: two workgroups share a CU, K and V
 // tiles double-buffered.  W = 8: one workgroup per CU (still two waves per SIMD), tiles
 // triple-buffered so that each load has two tiles of time to land.
-template <typename T, int D, bool CAUSAL, int W>
-__global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
+template <typename T, int D, bool CAUSAL, int W, bool SPLIT, typename P>
+__device__ __forceinline__ void fa_fwd_body(const P &p)
 {
     constexpr int kBM = 32 * W, kWaves = W;
     constexpr int NBUF = W == 8 ? 3 : 2;
@@ -155,12 +174,37 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
 
     // ---- A1: which (b, h, query tile) this workgroup computes
     const long long L = xcd_remap(blockIdx.x, p.total);
-    const TileCoord tc = logical_tile(L, p.Hq, p.Hkv, p.n_qt, CAUSAL);
+    TileCoord tc;
+    int rank = 0, split = 0, n_split = 1;
+    if constexpr (SPLIT) {
+        // logical order: (b, kv head), then query-tile rank with its shares, then the group's heads
+        const int g = p.Hq / p.Hkv;
+        const int hg = (int)(L % g);
+        const long long rest = L / g;
+        const int j = (int)(rest % p.wg_per_head);
+        const long long bhk = rest / p.wg_per_head;
+        int lo = 0, hi = p.n_qt;  // prefix[lo] <= j < prefix[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.prefix[mid] <= j) lo = mid; else hi = mid;
+        }
+        rank = lo;
+        split = j - p.prefix[lo];
+        n_split = p.prefix[lo + 1] - p.prefix[lo];
+        tc.b = (int)(bhk / p.Hkv);
+        tc.h = (int)(bhk % p.Hkv) * g + hg;
+        tc.qt = CAUSAL ? p.n_qt - 1 - rank : rank;
+    } else {
+        tc = logical_tile(L, p.Hq, p.Hkv, p.n_qt, CAUSAL);
+    }
     const int g = p.Hq / p.Hkv;
     const int hk = tc.h / g;
     const int m0 = tc.qt * kBM;
     const int M = p.M, N = p.N;
     const KvRange kr = kv_range(m0, kBM, kBN, M, N, CAUSAL);
+    // key tiles [t0, t0 + n_tiles) of the query tile's visible range are this workgroup's
+    const int t0 = split * kr.n_tiles / n_split;
+    const int n_tiles = (split + 1) * kr.n_tiles / n_split - t0;
 
     const T *qg = (const T *)p.q + ((size_t)tc.b * p.Hq + tc.h) * (size_t)M * D;
     const T *kg = (const T *)p.k + ((size_t)tc.b * p.Hkv + hk) * (size_t)N * D;
@@ -194,7 +238,10 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
     constexpr int TILE_GBYTES = kBN * D * (int)sizeof(T);
     lds_u8 *const sink = smem + NBUF * (K_TILE + V_TILE);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const long long kv_bytes = (long long)N * D * (long long)sizeof(T);
+    // loads of tiles past this workgroup's share (the pipeline runs ahead) read as zero
+    const long long kv_bytes_all = (long long)N * D * (long long)sizeof(T);
+    const long long kv_bytes = (long long)(t0 + n_tiles) * TILE_GBYTES < kv_bytes_all
+                                   ? (long long)(t0 + n_tiles) * TILE_GBYTES : kv_bytes_all;
     unsigned k_src[KI], v_src[VI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -217,7 +264,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
                                                  0x00020000);
     };
     auto load_k = [&](int t, int buf) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, t);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, t0 + t);
         lds_u8 *dst = smem + buf * K_TILE;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
@@ -226,7 +273,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         }
     };
     auto load_v = [&](int t, int buf) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, t);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, t0 + t);
         lds_u8 *dst = smem + NBUF * K_TILE + buf * V_TILE;
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
@@ -267,7 +314,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
 
     // mask (unless `none`) the scores of tile t, then return their in-lane max
     auto mask_max = [&](int t, f32x16 (&sc)[KB], bool none = false) {
-        const int n0 = t * kBN;
+        const int n0 = (t0 + t) * kBN;
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -430,14 +477,10 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
     };
 
 
-    // Software pipeline over key tiles.  K is staged one tile ahead of V: iteration t reads
-    // K_{t+1} and V_t from LDS while the loads of K_{t+2} and V_{t+1} fill the buffers that
-    // iteration t-1 finished reading, so one barrier per tile suffices.
     // Software pipeline over key tiles.  Iteration t reads K_{t+1} (scores of the next tile)
     // and V_t from LDS, and issues the loads of K_{t+NBUF} and V_{t+NBUF-1} into the buffers
     // that iteration t-1 finished reading; one barrier per tile publishes the loads issued
     // NBUF-2 iterations earlier.
-    const int n_tiles = kr.n_tiles;
     f32x16 s_cur[KB], s_nxt[KB];
     float mt_pending = -INFINITY;  // in-lane max of the scores whose running-max update is pending
     if (n_tiles > 0) {
@@ -453,7 +496,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         }
         __syncthreads();
         scores(0, s_cur);
-        mt_pending = mask_max(0, s_cur, kr.n_full > 0);
+        mt_pending = mask_max(0, s_cur, t0 < kr.n_full);
         __syncthreads();  // every wave has read K_0 before its buffer is refilled
     }
     int kb_next = 1 % NBUF, vb_cur = 0, b_load = 0;  // buffers of K_{t+1}, V_t, and of the loads (t % NBUF)
@@ -465,7 +508,7 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
         float psum = 0.f;
         float mt = step(std::true_type{}, kb_next, vb_cur, nxt, cur, mt_pending, psum);
         l_part += psum;
-        if (t + 1 >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
+        if (t0 + t + 1 >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
         mt_pending = mt;
         if constexpr (NBUF == 3)
             wait_loads(Keep1{});
@@ -507,24 +550,96 @@ __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
     }
     if (qvalid) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        T *og = (T *)p.o + (((size_t)tc.b * p.Hq + tc.h) * (size_t)M + qrow) * D;
+        const float lse = l_tot > 0.f ? (m_run * c + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+        const size_t row = ((size_t)tc.b * p.Hq + tc.h) * (size_t)M + qrow;
+        bool partial = false;
+        if constexpr (SPLIT) partial = n_split > 1;
+        if (partial) {  // this share's normalised fp32 output and lse, for the merge
+            if constexpr (SPLIT) {
+                const size_t slot =
+                    (((size_t)tc.b * p.Hq + tc.h) * p.slots + p.prefix[rank] + split) * p.slot_rows + (qrow - m0);
+                f32x4 *dst = (f32x4 *)(p.ws_o + slot * D);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            u32x4 w0, w1;
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                w0[r] = Elem<T>::pack2(oacc[db][2 * r] * inv, oacc[db][2 * r + 1] * inv);
-                w1[r] = Elem<T>::pack2(oacc[db][8 + 2 * r] * inv, oacc[db][8 + 2 * r + 1] * inv);
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const f32x4 w4 = {oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv,
+                                          oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv};
+                        dst[(db * 32 + hh * 16) / 4 + r4] = w4;
+                    }
+                if (hh == 0) p.ws_lse[slot] = lse;
             }
-            u32x4 *dst = (u32x4 *)(og + db * 32 + hh * 16);
-            dst[0] = w0;
-            dst[1] = w1;
-        }
-        if (hh == 0) {
-            const float lse2 = l_tot > 0.f ? m_run * c + __builtin_log2f(l_tot) : -INFINITY;
-            p.lse[((size_t)tc.b * p.Hq + tc.h) * (size_t)M + qrow] = lse2 * 0.69314718055994530942f;
+        } else {
+            T *og = (T *)p.o + row * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                u32x4 w0, w1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    w0[r] = Elem<T>::pack2(oacc[db][2 * r] * inv, oacc[db][2 * r + 1] * inv);
+                    w1[r] = Elem<T>::pack2(oacc[db][8 + 2 * r] * inv, oacc[db][8 + 2 * r + 1] * inv);
+                }
+                u32x4 *dst = (u32x4 *)(og + db * 32 + hh * 16);
+                dst[0] = w0;
+                dst[1] = w1;
+            }
+            if (hh == 0) p.lse[row] = lse;
         }
     }
+}
+
+template <typename T, int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
+{
+    fa_fwd_body<T, D, CAUSAL, W, false>(p);
+}
+
+// one share of a query tile's keys (key-split mode)
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_fwd_split_kernel(SplitParams p)
+{
+    fa_fwd_body<T, D, CAUSAL, 4, true>(p);
+}
+
+// Merge of the key shares of the split query tiles: with share lse_s (natural log) and
+// normalised share output O_s, lse = log sum_s exp(lse_s) and O = sum_s exp(lse_s - lse) O_s.
+// A share that saw no key of a row has lse_s = -inf and weight 0; a row no share saw gets
+// O = 0 and lse = -inf.  D/4 lanes per row, 4 columns each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(SplitParams p)
+{
+    constexpr int BM = 128, LPR = D / 4, RPB = 256 / LPR;
+    const int SR = p.slot_rows;
+    const long long per_bh = (long long)p.n_split_ranks * SR;
+    const long long r = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    if (r >= (long long)p.B * p.Hq * per_bh) return;
+    const int col = (threadIdx.x % LPR) * 4;
+    const long long bh = r / per_bh;
+    const int rem = (int)(r % per_bh), rank = rem / SR, ri = rem % SR;
+    const int i = (p.causal ? p.n_qt - 1 - rank : rank) * BM + ri;
+    if (i >= p.M) return;
+    const int base = p.prefix[rank], ns = p.prefix[rank + 1] - base;
+    const size_t s0 = ((size_t)bh * p.slots + base) * SR + ri;  // share s is slot s0 + s * SR
+    float m = -INFINITY;
+    for (int s = 0; s < ns; ++s) m = fmaxf(m, p.ws_lse[s0 + (size_t)s * SR]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+        for (int s = 0; s < ns; ++s) {
+            const size_t slot = s0 + (size_t)s * SR;
+            const float w = __expf(p.ws_lse[slot] - m);
+            wsum += w;
+            const f32x4 os = *(const f32x4 *)(p.ws_o + slot * D + col);
+            acc += w * os;
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const size_t row = (size_t)bh * p.M + i;
+    u32x2 w;
+    w[0] = Elem<T>::pack2(acc[0] * inv, acc[1] * inv);
+    w[1] = Elem<T>::pack2(acc[2] * inv, acc[3] * inv);
+    *(u32x2 *)((T *)p.o + row * D + col) = w;
+    if (col == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ host side
@@ -561,6 +676,125 @@ static hipError_t launch_t(const Params &p, int D, int W, bool causal, hipStream
 {
     if (D == 128) return W == 8 ? launch_w<T, 128, 8>(p, causal, stream) : launch_w<T, 128, 4>(p, causal, stream);
     return W == 8 ? launch_w<T, 64, 8>(p, causal, stream) : launch_w<T, 64, 4>(p, causal, stream);
+}
+
+// ---- key-split mode (4-wave workgroups, 128-row query tiles)
+
+constexpr int kSplitBM = 128;
+constexpr int kSplitTargetWgs = 512;  // two 4-wave workgroups per CU
+constexpr int kSplitMinTiles = 8;     // smallest share the automatic plan hands one workgroup
+constexpr int kSplitMinRange = 32;    // the automatic plan splits only query tiles this long or longer
+
+struct SplitPlan {
+    SplitParams sp;
+    int tiles;          // key tiles per share (the largest a workgroup gets)
+    size_t ws_bytes;    // workspace the partial results need (0: no tile is split)
+    size_t ws_o_offset; // byte offset of the partial outputs inside the workspace
+};
+
+// Shares per query tile: with at most `tiles` key tiles a share, a tile visiting n key tiles
+// gets ceil(n / tiles) shares.  tiles <= 0 asks for the automatic choice: no split when the
+// plain 4-wave grid already has kSplitTargetWgs workgroups or no query tile visits
+// kSplitMinRange key tiles (the partial results' round trip and the merge launch would cost
+// more than the balance gains), else the total key-tile work spread over about
+// kSplitTargetWgs workgroups, at least kSplitMinTiles tiles each.
+static int split_plan(int B, int Hq, int M, int N, int D, bool causal, int tiles, SplitPlan *pl)
+{
+    const int n_qt = (M + kSplitBM - 1) / kSplitBM;
+    if (n_qt > kMaxSplitQt) return FA_ERR_UNSUPPORTED;
+    int nt[kMaxSplitQt];
+    long long total_tiles = 0;
+    int max_tiles = 1;
+    for (int r = 0; r < n_qt; ++r) {
+        const int qt = causal ? n_qt - 1 - r : r;
+        nt[r] = kv_range(qt * kSplitBM, kSplitBM, kBN, M, N, causal).n_tiles;
+        total_tiles += nt[r];
+        if (nt[r] > max_tiles) max_tiles = nt[r];
+    }
+    const long long heads = (long long)B * Hq;
+    if (tiles <= 0) {
+        if (heads * n_qt >= kSplitTargetWgs || max_tiles < kSplitMinRange) {
+            tiles = max_tiles;
+        } else {
+            const long long t = (heads * total_tiles + kSplitTargetWgs - 1) / kSplitTargetWgs;
+            tiles = (int)(t < kSplitMinTiles ? kSplitMinTiles : (t > max_tiles ? max_tiles : t));
+        }
+    }
+    SplitParams &sp = pl->sp;
+    sp.prefix[0] = 0;
+    sp.n_split_ranks = 0;
+    for (int r = 0; r < n_qt; ++r) {
+        const int ns = nt[r] > tiles ? (nt[r] + tiles - 1) / tiles : 1;
+        sp.prefix[r + 1] = sp.prefix[r] + ns;
+        if (ns > 1) {
+            if (sp.n_split_ranks != r) return FA_ERR_INVALID_ARG;  // shares must not grow with the rank
+            sp.n_split_ranks = r + 1;
+        }
+    }
+    sp.n_qt = n_qt;
+    sp.wg_per_head = sp.prefix[n_qt];
+    sp.slots = sp.prefix[sp.n_split_ranks];
+    sp.causal = causal ? 1 : 0;
+    sp.slot_rows = M < kSplitBM ? M : kSplitBM;
+    sp.total = heads * sp.wg_per_head;
+    pl->tiles = tiles;
+    const size_t rows = (size_t)heads * sp.slots * sp.slot_rows;
+    pl->ws_o_offset = (rows * sizeof(float) + 255) & ~(size_t)255;
+    pl->ws_bytes = sp.slots ? pl->ws_o_offset + rows * D * sizeof(float) : 0;
+    return FA_OK;
+}
+
+template <typename T, int D>
+static hipError_t launch_split_d(const SplitParams &p, bool causal, hipStream_t stream)
+{
+    dim3 grid((unsigned)p.total), block(256);
+    if (causal)
+        hipLaunchKernelGGL((fa_fwd_split_kernel<T, D, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_split_kernel<T, D, false>), grid, block, 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.slots == 0) return e;
+    constexpr int RPB = 256 / (D / 4);
+    const long long rows = (long long)p.B * p.Hq * p.n_split_ranks * p.slot_rows;
+    hipLaunchKernelGGL((fa_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_split(const SplitParams &p, int D, bool causal, hipStream_t stream)
+{
+    return D == 128 ? launch_split_d<T, 128>(p, causal, stream) : launch_split_d<T, 64>(p, causal, stream);
+}
+
+// argument checks shared by the entry points; fills the sizes of p
+static int check_args(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
+                      int N, int D, float scale, int dtype, Params *p)
+{
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+    // element counts must fit in int64 (they do for any int sizes below 2^15 each; check anyway)
+    const double nq = (double)B * Hq * M * D, nk = (double)B * Hkv * N * D;
+    if (nq > 9.0e18 || nk > 9.0e18) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    // K and V of one (b, kv head) are addressed with 32-bit buffer offsets
+    if ((long long)N * D * 2 > 0x7fff0000LL) return FA_ERR_UNSUPPORTED;
+    const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
+    if (align & 15u) return FA_ERR_UNSUPPORTED;
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->o = o;
+    p->lse = lse;
+    p->B = B;
+    p->Hq = Hq;
+    p->Hkv = Hkv;
+    p->M = M;
+    p->N = N;
+    p->c = scale * 1.44269504088896340736f;  // log2(e)
+    return FA_OK;
 }
 
 }  // namespace fa
@@ -619,41 +853,59 @@ int fa_schedule(int B, int Hq, int Hkv, int M, int D, int causal, long long wg, 
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M, int N,
            int D, float scale, int causal, int dtype, void *stream)
 {
-    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
-    if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
-    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
-    // element counts must fit in int64 (they do for any int sizes below 2^15 each; check anyway)
-    const double nq = (double)B * Hq * M * D, nk = (double)B * Hkv * N * D;
-    if (nq > 9.0e18 || nk > 9.0e18) return FA_ERR_INVALID_ARG;
+    fa::Params p;
+    int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, dtype, &p);
+    if (rc != FA_OK) return rc;
     int BM, BN;
     if (fa::tile_shape(B, Hq, M, D, &BM, &BN) != FA_OK) return FA_ERR_UNSUPPORTED;
-    // K and V of one (b, kv head) are addressed with 32-bit buffer offsets
-    if ((long long)N * D * 2 > 0x7fff0000LL) return FA_ERR_UNSUPPORTED;
-    const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
-    if (align & 15u) return FA_ERR_UNSUPPORTED;
-
-    fa::Params p;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
-    p.lse = lse;
-    p.B = B;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.M = M;
-    p.N = N;
     p.n_qt = (M + BM - 1) / BM;
     p.total = (long long)B * Hq * p.n_qt;
     if (p.total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;  // one-dimensional grid limit
-    p.c = scale * 1.44269504088896340736f;                    // log2(e)
 
     hipStream_t s = (hipStream_t)stream;
     const int W = BM / 32;
     hipError_t err = dtype == FA_F16 ? fa::launch_t<_Float16>(p, D, W, causal != 0, s)
                                      : fa::launch_t<__bf16>(p, D, W, causal != 0, s);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_splitkv_plan(int B, int Hq, int Hkv, int M, int N, int D, int causal, int tiles_per_split, int *tiles_used,
+                    long long *workgroups, size_t *workspace_bytes)
+{
+    if (!tiles_used || !workgroups || !workspace_bytes) return FA_ERR_INVALID_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 || D <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    fa::SplitPlan pl;
+    const int rc = fa::split_plan(B, Hq, M, N, D, causal != 0, tiles_per_split, &pl);
+    if (rc != FA_OK) return rc;
+    *tiles_used = pl.tiles;
+    *workgroups = pl.sp.total;
+    *workspace_bytes = pl.ws_bytes;
+    return FA_OK;
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
+                   int N, int D, float scale, int causal, int dtype, int tiles_per_split, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    fa::SplitPlan pl;
+    int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, dtype, &pl.sp);
+    if (rc != FA_OK) return rc;
+    rc = fa::split_plan(B, Hq, M, N, D, causal != 0, tiles_per_split, &pl);
+    if (rc != FA_OK) return rc;
+    if (pl.sp.total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (pl.ws_bytes) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return FA_ERR_INVALID_ARG;
+        if ((uintptr_t)workspace & 255u) return FA_ERR_UNSUPPORTED;
+        pl.sp.ws_lse = (float *)workspace;
+        pl.sp.ws_o = (float *)((char *)workspace + pl.ws_o_offset);
+    } else {
+        pl.sp.ws_lse = nullptr;
+        pl.sp.ws_o = nullptr;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err = dtype == FA_F16 ? fa::launch_split<_Float16>(pl.sp, D, causal != 0, s)
+                                     : fa::launch_split<__bf16>(pl.sp, D, causal != 0, s);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

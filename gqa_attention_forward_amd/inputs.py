@@ -56,6 +56,14 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Small-grid shapes for the key-split forward: decode (one query row per head against an
+# 8k-key cache) and a short 64-row query chunk, both GQA with 4 query heads per KV head.
+SMALL_GRID_WORKLOADS = {
+    "decode_gqa_8k": Workload("decode_gqa_8k", 8, 32, 8, 1, 8192, 128, torch.bfloat16, True, 5),
+    "short_query_gqa_8k": Workload("short_query_gqa_8k", 4, 32, 8, 64, 8192, 128, torch.float16, True, 6),
+}
+ALL_WORKLOADS = {**WORKLOADS, **SMALL_GRID_WORKLOADS}
+
 
 def make_inputs(w: Workload, device: str | torch.device = "cpu"):
     """Returns (q, k, v, n_peaky_rows). The draw always happens on the CPU generator."""

@@ -31,6 +31,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -78,6 +80,48 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 
 /* Human-readable text for a return code (static storage; never NULL). */
 const char *fa_strerror(int code);
+
+/*
+ * Key-split forward, for grids too small to fill the GPU (few heads or query tiles, decode-like M).
+ *
+ * The key tiles a 128-row query tile visits are divided into even shares of at most
+ * `tiles_per_split` tiles, one workgroup per share.  Each share's workgroup runs the same online
+ * softmax over its keys and leaves its normalised partial output O_s and natural-log partial
+ * lse_s in the workspace; a merge kernel then forms, per row,
+ *     lse = ln sum_s exp(lse_s),   O = sum_s exp(lse_s - lse) O_s,
+ * which is the online-softmax combination step of "从零开始写Qwen3" (FlashAttention derivation
+ * article), section "在线softmax", applied to two or more disjoint key sets at once: the result
+ * equals fa_fwd's up to fp32 rounding order.  A share whose keys a row cannot see has
+ * lse_s = -inf and weight 0.  Query tiles with a single share write O and lse directly.
+ * Choosing the share count from the grid size follows the small-grid rule of
+ * "lab3：GDN Prefill 前向优化", sections "TMA, DV 分块" and "GVA 感知的 block_DV" (a finer
+ * work split only when the plain grid leaves CUs idle).
+ *
+ * fa_splitkv_plan: host-only.  tiles_per_split > 0 is used as given; <= 0 asks for the automatic
+ *   choice (no split when the 4-wave grid already has 512 workgroups or no query tile visits 32
+ *   key tiles, else shares of the key-tile work spread over about 512 workgroups, at least 8
+ *   tiles each).  Writes the key tiles per share
+ *   actually used (*tiles_used), the workgroup count of the split kernel (*workgroups) and the
+ *   workspace size in bytes (*workspace_bytes; 0 when no query tile is split).  Returns FA_OK,
+ *   FA_ERR_INVALID_ARG (null pointer, non-positive size, Hq % Hkv != 0) or FA_ERR_UNSUPPORTED
+ *   (D not 64 or 128, more than 128 query tiles per head, i.e. M > 16384).
+ *
+ * fa_fwd_splitkv: arguments, layouts, determinism and error codes as fa_fwd, plus
+ *   tiles_per_split   as for fa_splitkv_plan (the plan is recomputed from the same arguments)
+ *   workspace         DEVICE memory owned by the caller, 256-byte aligned, at least the size
+ *                     fa_splitkv_plan reports (may be NULL when that size is 0); overwritten
+ *   workspace_bytes   its size
+ * Enqueues the split kernel and, when some query tile is split, the merge kernel, both on
+ * `stream`; returns without synchronising.  The workspace must not be used by another call
+ * until the merge has run (calls on one stream are ordered).  Returns FA_ERR_INVALID_ARG also
+ * for a missing or too small workspace, FA_ERR_UNSUPPORTED also for a workspace not 256-byte
+ * aligned or M > 16384.
+ */
+int fa_splitkv_plan(int B, int Hq, int Hkv, int M, int N, int D, int causal, int tiles_per_split, int *tiles_used,
+                    long long *workgroups, size_t *workspace_bytes);
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
+                   int N, int D, float scale, int causal, int dtype, int tiles_per_split, void *workspace,
+                   size_t workspace_bytes, void *stream);
 
 /*
  * Introspection of the launch plan (host-only, no GPU needed).  These report the tiling

@@ -58,3 +58,79 @@ def test_invalid_arguments(bad):
 @pytest.mark.parametrize("bad", [dict(D=96), dict(D=256), dict(D=32), dict(q=0x1008), dict(lse=0x5004)])
 def test_unsupported(bad):
     assert _call(**bad) == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ key-split forward plan
+
+def _brute_key_tiles(M, N, BM, BN, causal):
+    """Key tiles each 128-row query tile visits, from the mask definition itself (rank order:
+    longest first when causal)."""
+    tiles = []
+    for qt in range((M + BM - 1) // BM):
+        last = min(M, (qt + 1) * BM) - 1
+        seen = N if not causal else max(0, min(N, last + 1 + N - M))  # keys visible to the tile's last row
+        tiles.append((seen + BN - 1) // BN)
+    return tiles[::-1] if causal else tiles
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 16, 8, 1024, 1024, 128, True, 5), (1, 32, 8, 1, 8192, 128, True, 8), (1, 4, 1, 300, 77, 64, True, 1),
+    (1, 2, 2, 200, 333, 128, False, 2), (3, 2, 1, 1000, 1000, 64, True, 3), (1, 1, 1, 16384, 16384, 128, True, 40),
+])
+def test_splitkv_plan_matches_brute_force(shape):
+    B, Hq, Hkv, M, N, D, causal, tiles = shape
+    used, wgs, ws = fa.fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles)
+    assert used == tiles
+    shares = [(n + tiles - 1) // tiles if n > tiles else 1 for n in _brute_key_tiles(M, N, 128, 64, causal)]
+    assert wgs == B * Hq * sum(shares)
+    slots = sum(s for s in shares if s > 1)
+    rows = B * Hq * slots * min(128, M)
+    assert ws == (0 if slots == 0 else ((rows * 4 + 255) // 256) * 256 + rows * D * 4)
+
+
+def test_splitkv_auto_policy():
+    # the 4-wave grid already has 512 workgroups: no split
+    for B, Hq, M in [(4, 32, 512), (1, 32, 16384), (8, 64, 128)]:
+        used, wgs, ws = fa.fa_splitkv_plan(B, Hq, Hq, M, 4096, 128, True, 0)
+        assert ws == 0 and wgs == B * Hq * ((M + 127) // 128)
+    # no query tile visits 32 key tiles: no split (the 1k causal workload)
+    used, wgs, ws = fa.fa_splitkv_plan(2, 16, 8, 1024, 1024, 128, True, 0)
+    assert ws == 0 and wgs == 2 * 16 * 8
+    # decode-like: one query row per head, 8192 keys -> 128 key tiles; 32 heads spread over 512 workgroups
+    used, wgs, ws = fa.fa_splitkv_plan(1, 32, 8, 1, 8192, 128, True, 0)
+    assert used == 8 and wgs == 512 and ws > 0
+    # never below 8 key tiles a share
+    used, wgs, ws = fa.fa_splitkv_plan(1, 2, 1, 64, 2048, 64, False, 0)
+    assert used == 8 and wgs == 2 * 4
+
+
+SPLIT_GOOD = dict(GOOD, tiles=1, ws=0x100000, ws_bytes=1 << 30)
+
+
+def _call_split(**kw):
+    a = dict(SPLIT_GOOD)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["M"], a["N"],
+                             a["D"], a["scale"], a["causal"], a["dtype"], a["tiles"], a["ws"], a["ws_bytes"],
+                             a["stream"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(q=None), dict(lse=None), dict(B=0), dict(Hq=3, Hkv=2), dict(scale=0.0), dict(dtype=2),
+    dict(M=200, N=1000, ws=None), dict(M=200, N=1000, ws_bytes=1024),
+])
+def test_splitkv_invalid_arguments(bad):
+    assert _call_split(**bad) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(D=96), dict(q=0x1008), dict(M=200, N=1000, ws=0x100080),
+                                 dict(M=16385, N=64)])
+def test_splitkv_unsupported(bad):
+    assert _call_split(**bad) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_splitkv_plan_invalid():
+    with pytest.raises(fa.FaError):
+        fa.fa_splitkv_plan(1, 3, 2, 16, 16, 64, True)
+    with pytest.raises(fa.FaError):
+        fa.fa_splitkv_plan(1, 2, 1, 16385, 16, 64, True)

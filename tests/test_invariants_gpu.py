@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _fwd(q, k, v, causal, scale=None):
-    o, lse = fa.attention_forward(q, k, v, causal=causal, scale=scale)
+    o, lse = fa.attention_forward(q, k, v, causal=causal, scale=scale, split_kv=False)
     torch.cuda.synchronize()
     return o, lse
 
@@ -97,6 +97,6 @@ def test_respects_stream():
     o_ref, l_ref = _fwd(q, k, v, True)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        o, lse = fa.attention_forward(q, k, v, causal=True)
+        o, lse = fa.attention_forward(q, k, v, causal=True, split_kv=False)
     s.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)

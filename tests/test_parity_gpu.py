@@ -21,7 +21,7 @@ LSE_TOL = 1e-3
 
 def _run_gpu(q, k, v, causal, scale):
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
-    o, lse = fa.attention_forward(dq, dk, dv, causal=causal, scale=scale)
+    o, lse = fa.attention_forward(dq, dk, dv, causal=causal, scale=scale, split_kv=False)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
