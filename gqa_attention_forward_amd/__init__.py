@@ -143,7 +143,8 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
     q [B,Hq,M,D], k/v [B,Hkv,N,D] (fp16 or bf16).  Returns (o [B,Hq,M,D], lse [B,Hq,M] fp32).
 
     split_kv: "auto" runs the key-split forward when its plan splits some query tile (small
-    grids) and fa_fwd otherwise; False always runs fa_fwd; an int > 0 runs the key-split forward
+    grids) or when M < 128 with grouped KV heads (the key-split kernel then stacks the query
+    heads of a group into one tile's rows), and fa_fwd otherwise; False always runs fa_fwd; an int > 0 runs the key-split forward
     with at most that many key tiles per share.  The split workspace comes from torch's caching
     allocator.  Kernels are enqueued on `stream` (default: torch's current stream) and not
     waited for."""
@@ -177,7 +178,7 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
         M_ok = M <= 128 * 128  # the split plan describes at most 128 query tiles per head
         if M_ok and D in (64, 128):
             _, _, ws_bytes = fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles)
-            if ws_bytes > 0 or split_kv != "auto":
+            if ws_bytes > 0 or split_kv != "auto" or (M < 128 and Hq > Hkv):
                 ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
                 rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
                                     Hkv, M, N, D, scale, causal, _dtype_code(q), tiles, ws.data_ptr(), ws_bytes, stream)

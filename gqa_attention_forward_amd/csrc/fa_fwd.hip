@@ -132,15 +132,19 @@ struct Params {
 // workspace, and a merge kernel combines them.  A query tile with one share writes O and lse
 // directly.  Query tiles are taken in rank order (longest first when causal), so the shares
 // per tile never grow with the rank and the split tiles are the ranks [0, n_split_ranks).
+// Rows come in units of R = pack * M: with pack = 1 a unit is one query head; with pack = g
+// (short queries, M < 128) a unit stacks the g query heads of one KV group, row r being query
+// r % M of head r / M, so that one tile's MFMA rows are not mostly empty.
 constexpr int kMaxSplitQt = 128;  // query tiles per (b, h) the split plan can describe
 struct SplitParams : Params {
     int wg_per_head;    // workgroups per (b, h): prefix[n_qt]
     int slots;          // partial slots per (b, h): prefix[n_split_ranks]
     int n_split_ranks;
     int causal;
-    int slot_rows;      // rows a slot holds: min(BM, M)
-    float *ws_lse;      // [B*Hq][slots][slot_rows]
-    float *ws_o;        // [B*Hq][slots][slot_rows][D]
+    int pack;           // 1, or Hq / Hkv
+    int slot_rows;      // rows a slot holds: min(BM, R)
+    float *ws_lse;      // [units][slots][slot_rows], units = B * Hq / pack
+    float *ws_o;        // [units][slots][slot_rows][D]
     int prefix[kMaxSplitQt + 1];  // workgroups of the query-tile ranks below r
 };
 
@@ -174,13 +178,16 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
 
     // ---- A1: which (b, h, query tile) this workgroup computes
     const long long L = xcd_remap(blockIdx.x, p.total);
-    TileCoord tc;
+    TileCoord tc;  // tc.h: the (first) query head of the workgroup's unit
     int rank = 0, split = 0, n_split = 1;
+    int R = p.M;           // rows of the unit
+    long long unit = 0;    // unit index (key-split mode)
     if constexpr (SPLIT) {
-        // logical order: (b, kv head), then query-tile rank with its shares, then the group's heads
+        // logical order: (b, kv head), then query-tile rank with its shares, then the group's units
         const int g = p.Hq / p.Hkv;
-        const int hg = (int)(L % g);
-        const long long rest = L / g;
+        const int gu = g / p.pack;  // units per KV group
+        const int hg = (int)(L % gu);
+        const long long rest = L / gu;
         const int j = (int)(rest % p.wg_per_head);
         const long long bhk = rest / p.wg_per_head;
         int lo = 0, hi = p.n_qt;  // prefix[lo] <= j < prefix[hi]
@@ -192,8 +199,10 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         split = j - p.prefix[lo];
         n_split = p.prefix[lo + 1] - p.prefix[lo];
         tc.b = (int)(bhk / p.Hkv);
-        tc.h = (int)(bhk % p.Hkv) * g + hg;
+        tc.h = (int)(bhk % p.Hkv) * g + hg * p.pack;
         tc.qt = CAUSAL ? p.n_qt - 1 - rank : rank;
+        unit = bhk * gu + hg;
+        R = p.pack * p.M;
     } else {
         tc = logical_tile(L, p.Hq, p.Hkv, p.n_qt, CAUSAL);
     }
@@ -201,24 +210,29 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     const int hk = tc.h / g;
     const int m0 = tc.qt * kBM;
     const int M = p.M, N = p.N;
-    const KvRange kr = kv_range(m0, kBM, kBN, M, N, CAUSAL);
+    const KvRange kr = SPLIT ? unit_kv_range(m0, kBM, kBN, M, N, R, CAUSAL) : kv_range(m0, kBM, kBN, M, N, CAUSAL);
     // key tiles [t0, t0 + n_tiles) of the query tile's visible range are this workgroup's
     const int t0 = split * kr.n_tiles / n_split;
     const int n_tiles = (split + 1) * kr.n_tiles / n_split - t0;
 
-    const T *qg = (const T *)p.q + ((size_t)tc.b * p.Hq + tc.h) * (size_t)M * D;
     const T *kg = (const T *)p.k + ((size_t)tc.b * p.Hkv + hk) * (size_t)N * D;
     const T *vg = (const T *)p.v + ((size_t)tc.b * p.Hkv + hk) * (size_t)N * D;
 
-    const int qrow = m0 + wave * 32 + ql;  // this lane's query row
-    const bool qvalid = qrow < M;
+    const int qrow = m0 + wave * 32 + ql;  // this lane's row of the unit
+    const bool qvalid = qrow < R;
+    int qpos = qrow, qhead = tc.h;           // its query position and head
+    if constexpr (SPLIT) {
+        qpos = qrow % M;
+        qhead = tc.h + qrow / M;
+    }
+    const T *qg = (const T *)p.q + (((size_t)tc.b * p.Hq + qhead) * (size_t)M + qpos) * D;  // read only if qvalid
 
     // ---- A2: the Q operand, resident in registers (B operand of S^T = K Q^T)
     u32x4 qreg[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         u32x4 z = {0u, 0u, 0u, 0u};
-        qreg[ks] = qvalid ? *(const u32x4 *)(qg + (size_t)qrow * D + ks * 16 + hh * 8) : z;
+        qreg[ks] = qvalid ? *(const u32x4 *)(qg + ks * 16 + hh * 8) : z;
     }
 
     // ---- A3: K and V tiles go from HBM straight into LDS: buffer loads whose destination is
@@ -299,7 +313,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     float m_run = -INFINITY;  // running max of the raw scores s (not scaled)
     float l_part = 0.f;       // running sum over this half's keys, relative to m_run
     const float c = p.c;
-    const int causal_lim = qrow + (N - M);  // last visible key of this row (causal)
+    const int causal_lim = qpos + (N - M);  // last visible key of this row (causal)
 
     // per-lane read bases: K slot ql of each 32-key block, unit hh of each 32-byte k-step
     const int k_rd = ql * KP + hh * 16;
@@ -551,13 +565,12 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     if (qvalid) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse = l_tot > 0.f ? (m_run * c + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
-        const size_t row = ((size_t)tc.b * p.Hq + tc.h) * (size_t)M + qrow;
+        const size_t row = ((size_t)tc.b * p.Hq + qhead) * (size_t)M + qpos;
         bool partial = false;
         if constexpr (SPLIT) partial = n_split > 1;
         if (partial) {  // this share's normalised fp32 output and lse, for the merge
             if constexpr (SPLIT) {
-                const size_t slot =
-                    (((size_t)tc.b * p.Hq + tc.h) * p.slots + p.prefix[rank] + split) * p.slot_rows + (qrow - m0);
+                const size_t slot = ((size_t)unit * p.slots + p.prefix[rank] + split) * p.slot_rows + (qrow - m0);
                 f32x4 *dst = (f32x4 *)(p.ws_o + slot * D);
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
@@ -609,17 +622,18 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_merge_kernel(SplitParams p)
 {
     constexpr int BM = 128, LPR = D / 4, RPB = 256 / LPR;
-    const int SR = p.slot_rows;
-    const long long per_bh = (long long)p.n_split_ranks * SR;
+    const int SR = p.slot_rows, units_per_b = p.Hq / p.pack;
+    const long long per_unit = (long long)p.n_split_ranks * SR;
     const long long r = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-    if (r >= (long long)p.B * p.Hq * per_bh) return;
+    if (r >= (long long)p.B * units_per_b * per_unit) return;
     const int col = (threadIdx.x % LPR) * 4;
-    const long long bh = r / per_bh;
-    const int rem = (int)(r % per_bh), rank = rem / SR, ri = rem % SR;
-    const int i = (p.causal ? p.n_qt - 1 - rank : rank) * BM + ri;
-    if (i >= p.M) return;
+    const long long unit = r / per_unit;
+    const int rem = (int)(r % per_unit), rank = rem / SR, ri = rem % SR;
+    const int rl = (p.causal ? p.n_qt - 1 - rank : rank) * BM + ri;  // row of the unit
+    if (rl >= p.pack * p.M) return;
+    const int b = (int)(unit / units_per_b), h = (int)(unit % units_per_b) * p.pack + rl / p.M, i = rl % p.M;
     const int base = p.prefix[rank], ns = p.prefix[rank + 1] - base;
-    const size_t s0 = ((size_t)bh * p.slots + base) * SR + ri;  // share s is slot s0 + s * SR
+    const size_t s0 = ((size_t)unit * p.slots + base) * SR + ri;  // share s is slot s0 + s * SR
     float m = -INFINITY;
     for (int s = 0; s < ns; ++s) m = fmaxf(m, p.ws_lse[s0 + (size_t)s * SR]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -634,7 +648,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(SplitParams p)
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const size_t row = (size_t)bh * p.M + i;
+    const size_t row = ((size_t)b * p.Hq + h) * p.M + i;
     u32x2 w;
     w[0] = Elem<T>::pack2(acc[0] * inv, acc[1] * inv);
     w[1] = Elem<T>::pack2(acc[2] * inv, acc[3] * inv);
@@ -698,20 +712,24 @@ struct SplitPlan {
 // kSplitMinRange key tiles (the partial results' round trip and the merge launch would cost
 // more than the balance gains), else the total key-tile work spread over about
 // kSplitTargetWgs workgroups, at least kSplitMinTiles tiles each.
-static int split_plan(int B, int Hq, int M, int N, int D, bool causal, int tiles, SplitPlan *pl)
+static int split_plan(int B, int Hq, int Hkv, int M, int N, int D, bool causal, int tiles, SplitPlan *pl)
 {
-    const int n_qt = (M + kSplitBM - 1) / kSplitBM;
+    // short queries: stack the query heads of a KV group into the rows of one unit
+    const int g = Hq / Hkv;
+    int pack = M < kSplitBM && g > 1 && ((long long)g * M + kSplitBM - 1) / kSplitBM <= kMaxSplitQt ? g : 1;
+    const int R = pack * M;
+    const int n_qt = (R + kSplitBM - 1) / kSplitBM;
     if (n_qt > kMaxSplitQt) return FA_ERR_UNSUPPORTED;
     int nt[kMaxSplitQt];
     long long total_tiles = 0;
     int max_tiles = 1;
     for (int r = 0; r < n_qt; ++r) {
         const int qt = causal ? n_qt - 1 - r : r;
-        nt[r] = kv_range(qt * kSplitBM, kSplitBM, kBN, M, N, causal).n_tiles;
+        nt[r] = unit_kv_range(qt * kSplitBM, kSplitBM, kBN, M, N, R, causal).n_tiles;
         total_tiles += nt[r];
         if (nt[r] > max_tiles) max_tiles = nt[r];
     }
-    const long long heads = (long long)B * Hq;
+    const long long heads = (long long)B * Hq / pack;  // units
     if (tiles <= 0) {
         if (heads * n_qt >= kSplitTargetWgs || max_tiles < kSplitMinRange) {
             tiles = max_tiles;
@@ -735,7 +753,8 @@ static int split_plan(int B, int Hq, int M, int N, int D, bool causal, int tiles
     sp.wg_per_head = sp.prefix[n_qt];
     sp.slots = sp.prefix[sp.n_split_ranks];
     sp.causal = causal ? 1 : 0;
-    sp.slot_rows = M < kSplitBM ? M : kSplitBM;
+    sp.pack = pack;
+    sp.slot_rows = R < kSplitBM ? R : kSplitBM;
     sp.total = heads * sp.wg_per_head;
     pl->tiles = tiles;
     const size_t rows = (size_t)heads * sp.slots * sp.slot_rows;
@@ -755,7 +774,7 @@ static hipError_t launch_split_d(const SplitParams &p, bool causal, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.slots == 0) return e;
     constexpr int RPB = 256 / (D / 4);
-    const long long rows = (long long)p.B * p.Hq * p.n_split_ranks * p.slot_rows;
+    const long long rows = (long long)p.B * (p.Hq / p.pack) * p.n_split_ranks * p.slot_rows;
     hipLaunchKernelGGL((fa_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -876,7 +895,7 @@ int fa_splitkv_plan(int B, int Hq, int Hkv, int M, int N, int D, int causal, int
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 || D <= 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
     fa::SplitPlan pl;
-    const int rc = fa::split_plan(B, Hq, M, N, D, causal != 0, tiles_per_split, &pl);
+    const int rc = fa::split_plan(B, Hq, Hkv, M, N, D, causal != 0, tiles_per_split, &pl);
     if (rc != FA_OK) return rc;
     *tiles_used = pl.tiles;
     *workgroups = pl.sp.total;
@@ -891,7 +910,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     fa::SplitPlan pl;
     int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, dtype, &pl.sp);
     if (rc != FA_OK) return rc;
-    rc = fa::split_plan(B, Hq, M, N, D, causal != 0, tiles_per_split, &pl);
+    rc = fa::split_plan(B, Hq, Hkv, M, N, D, causal != 0, tiles_per_split, &pl);
     if (rc != FA_OK) return rc;
     if (pl.sp.total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     if (pl.ws_bytes) {

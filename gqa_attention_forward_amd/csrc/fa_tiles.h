@@ -30,8 +30,8 @@ __host__ __device__ inline int clampi(long long x, long long lo, long long hi)
     return (int)(x < lo ? lo : (x > hi ? hi : x));
 }
 
-// Key tiles for the query tile whose first row is m0 (rows m0 .. m0+BM-1, clipped to M).
-__host__ __device__ inline KvRange kv_range(int m0, int BM, int BN, int M, int N, bool causal)
+// Key tiles for a query tile whose rows have query positions first .. last (first <= last).
+__host__ __device__ inline KvRange kv_range_rows(int first, int last, int BN, int M, int N, bool causal)
 {
     KvRange r;
     int n_whole = N / BN;  // key tiles with no ragged tail
@@ -40,17 +40,32 @@ __host__ __device__ inline KvRange kv_range(int m0, int BM, int BN, int M, int N
         r.n_full = n_whole;
         return r;
     }
-    long long last_row = (long long)(m0 + BM < M ? m0 + BM : M) - 1;
     long long off = (long long)N - M;
     // keys [0, hi) are visible to at least the last row of the tile
-    int hi = clampi(last_row + 1 + off, 0, N);
+    int hi = clampi((long long)last + 1 + off, 0, N);
     r.n_tiles = (hi + BN - 1) / BN;
-    // a tile [n0, n0+BN) needs no mask iff its last key is visible to the first row m0
-    int lo_keys = clampi((long long)m0 + 1 + off, 0, N);  // keys visible to row m0
+    // a tile [n0, n0+BN) needs no mask iff its last key is visible to the first row
+    int lo_keys = clampi((long long)first + 1 + off, 0, N);  // keys visible to the first row
     int nf = lo_keys / BN;
     r.n_full = nf < n_whole ? nf : n_whole;
     if (r.n_full > r.n_tiles) r.n_full = r.n_tiles;
     return r;
+}
+
+// Key tiles for the query tile whose first row is m0 (rows m0 .. m0+BM-1, clipped to M).
+__host__ __device__ inline KvRange kv_range(int m0, int BM, int BN, int M, int N, bool causal)
+{
+    return kv_range_rows(m0, (m0 + BM < M ? m0 + BM : M) - 1, BN, M, N, causal);
+}
+
+// Key tiles for rows m0 .. m0+BM-1 (clipped to R) of a unit of R = pack * M rows in which row r
+// is query position r % M of the unit's head r / M (pack query heads of one KV group stacked).
+// A tile that crosses from one head into the next holds both the last and the first position.
+__host__ __device__ inline KvRange unit_kv_range(int m0, int BM, int BN, int M, int N, int R, bool causal)
+{
+    const int r1 = (m0 + BM < R ? m0 + BM : R) - 1;
+    if (m0 / M == r1 / M) return kv_range_rows(m0 % M, r1 % M, BN, M, N, causal);
+    return kv_range_rows(0, M - 1, BN, M, N, causal);
 }
 
 // Linear workgroup id -> logical work index, so that logical indices that are contiguous

@@ -62,13 +62,15 @@ def test_unsupported(bad):
 
 # ------------------------------------------------------------ key-split forward plan
 
-def _brute_key_tiles(M, N, BM, BN, causal):
-    """Key tiles each 128-row query tile visits, from the mask definition itself (rank order:
-    longest first when causal)."""
+def _brute_key_tiles(M, N, BM, BN, causal, pack):
+    """Key tiles each 128-row query tile of a unit visits, from the mask definition itself: a unit
+    stacks `pack` query heads, its row r being query position r % M (rank order: longest first
+    when causal)."""
+    R = pack * M
     tiles = []
-    for qt in range((M + BM - 1) // BM):
-        last = min(M, (qt + 1) * BM) - 1
-        seen = N if not causal else max(0, min(N, last + 1 + N - M))  # keys visible to the tile's last row
+    for qt in range((R + BM - 1) // BM):
+        rows = range(qt * BM, min(R, (qt + 1) * BM))
+        seen = max(N if not causal else max(0, min(N, r % M + 1 + N - M)) for r in rows)
         tiles.append((seen + BN - 1) // BN)
     return tiles[::-1] if causal else tiles
 
@@ -76,15 +78,19 @@ def _brute_key_tiles(M, N, BM, BN, causal):
 @pytest.mark.parametrize("shape", [
     (2, 16, 8, 1024, 1024, 128, True, 5), (1, 32, 8, 1, 8192, 128, True, 8), (1, 4, 1, 300, 77, 64, True, 1),
     (1, 2, 2, 200, 333, 128, False, 2), (3, 2, 1, 1000, 1000, 64, True, 3), (1, 1, 1, 16384, 16384, 128, True, 40),
+    (4, 32, 8, 64, 8192, 128, True, 16), (1, 12, 1, 100, 700, 64, True, 2), (2, 8, 1, 33, 64, 128, True, 1),
+    (1, 16, 2, 127, 3000, 128, False, 5),
 ])
 def test_splitkv_plan_matches_brute_force(shape):
     B, Hq, Hkv, M, N, D, causal, tiles = shape
     used, wgs, ws = fa.fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles)
     assert used == tiles
-    shares = [(n + tiles - 1) // tiles if n > tiles else 1 for n in _brute_key_tiles(M, N, 128, 64, causal)]
-    assert wgs == B * Hq * sum(shares)
+    pack = Hq // Hkv if M < 128 else 1  # short queries: the heads of a KV group share tiles
+    units = B * Hq // pack
+    shares = [(n + tiles - 1) // tiles if n > tiles else 1 for n in _brute_key_tiles(M, N, 128, 64, causal, pack)]
+    assert wgs == units * sum(shares)
     slots = sum(s for s in shares if s > 1)
-    rows = B * Hq * slots * min(128, M)
+    rows = units * slots * min(128, pack * M)
     assert ws == (0 if slots == 0 else ((rows * 4 + 255) // 256) * 256 + rows * D * 4)
 
 
@@ -96,11 +102,14 @@ def test_splitkv_auto_policy():
     # no query tile visits 32 key tiles: no split (the 1k causal workload)
     used, wgs, ws = fa.fa_splitkv_plan(2, 16, 8, 1024, 1024, 128, True, 0)
     assert ws == 0 and wgs == 2 * 16 * 8
-    # decode-like: one query row per head, 8192 keys -> 128 key tiles; 32 heads spread over 512 workgroups
+    # decode-like: one query row per head, 8192 keys -> 128 key tiles; the 4 heads of each KV group
+    # share one tile, and the 8 groups' tiles are spread over 512 workgroups (but >= 8 tiles a share)
     used, wgs, ws = fa.fa_splitkv_plan(1, 32, 8, 1, 8192, 128, True, 0)
-    assert used == 8 and wgs == 512 and ws > 0
-    # never below 8 key tiles a share
+    assert used == 8 and wgs == 8 * 16 and ws > 0
+    # never below 8 key tiles a share (the two heads of the group stacked in one 128-row tile)
     used, wgs, ws = fa.fa_splitkv_plan(1, 2, 1, 64, 2048, 64, False, 0)
+    assert used == 8 and wgs == 4
+    used, wgs, ws = fa.fa_splitkv_plan(1, 2, 2, 64, 2048, 64, False, 0)  # no grouping: one tile per head
     assert used == 8 and wgs == 2 * 4
 
 

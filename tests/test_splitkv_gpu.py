@@ -54,6 +54,12 @@ SHAPES = [
     (2, 8, 2, 16, 3000, 64, True, torch.float16, 0),        # short M, automatic plan
     (1, 8, 8, 64, 2048, 128, False, torch.float16, 0),
     (1, 2, 1, 1000, 600, 128, True, torch.bfloat16, 2),     # M > N: early rows empty, later rows split
+    # M < 128 with grouped KV heads: the group's query heads are stacked in one tile's rows
+    (1, 12, 1, 100, 700, 64, True, torch.bfloat16, 2),      # tiles straddle head boundaries, causal
+    (2, 8, 1, 33, 64, 128, True, torch.float16, 1),
+    (1, 6, 2, 50, 40, 128, True, torch.bfloat16, 1),        # M > N: the first 10 rows of every head empty
+    (1, 16, 2, 127, 3000, 128, False, torch.float16, 5),
+    (16, 32, 8, 64, 512, 128, True, torch.float16, 0),      # automatic: stacked heads, no split
 ]
 
 
