@@ -50,6 +50,8 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--layout", choices=["bhsd", "bshd"], default="bhsd",
+                    help="memory layout of q, k, v, o: contiguous [B,H,S,D] or [B,S,H,D] buffers (strided path)")
     ap.add_argument("--split-kv", default="auto",
                     help="'auto' (key-split forward for small grids), 'off', or key tiles per share")
     return ap.parse_args()
@@ -197,6 +199,8 @@ def main():
     for name in names:
         w = WORKLOADS[name]
         q, k, v, _ = make_inputs(w, device="cuda")
+        if args.layout == "bshd":  # the same values in [B, S, H, D] buffers, passed as [B, H, S, D] views
+            q, k, v = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
         torch.cuda.synchronize()
         wall, durs, o, lse = time_gpu(fa, w, q, k, v, args.steps, args.warmup, split_kv)
         path = "fa_fwd"
@@ -213,7 +217,7 @@ def main():
         f_, m_, _ = fa.fa_tile_counts(w.M, w.N, bm, bn, w.causal)
         issued = 4 * bm * bn * w.D * (f_ + m_) * w.B * w.Hq
         line = {
-            "workload": name, "path": path, "tflops": round(tflops, 2), "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "workload": name, "layout": args.layout, "path": path, "tflops": round(tflops, 2), "kernel_avg_us": round(avg_ms * 1e3, 2),
             "kernel_median_us": round(durs[len(durs) // 2] * 1e3, 2), "kernel_min_us": round(durs[0] * 1e3, 2),
             "pct_mfma_peak": round(100 * achieved / MFMA_PEAK_TFLOPS, 2),
             "issued_mfma_tflops": round(issued / (avg_ms * 1e-3) / 1e12, 2),
@@ -236,7 +240,7 @@ def main():
                 "vs_baseline": None,
                 "dtype": "bf16" if w.dtype == torch.bfloat16 else "f16",
                 "data": "synthetic",
-                "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "M": w.M, "N": w.N, "D": w.D,
+                "config": {"workload": name, "layout": args.layout, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "M": w.M, "N": w.N, "D": w.D,
                            "causal": w.causal, "seed": w.seed, "peaky_k_rows": w.peak_rate,
                            "parallelism": "single GPU"},
                 "pct_of_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 3),

@@ -7,7 +7,9 @@ fallback: if ``libfa.so`` is missing or cannot be loaded, every call raises.
 Functions with the C ABI's names take raw device pointers and sizes:
 
     fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream)
+    fa_fwd_strided(q_ptr, ..., D, q_strides, k_strides, v_strides, o_strides, scale, causal, dtype, stream)
     fa_fwd_splitkv(..., dtype, tiles_per_split, workspace_ptr, workspace_bytes, stream)
+    fa_fwd_splitkv_strided(..., D, q_strides, ..., o_strides, scale, ..., workspace_bytes, stream)
     fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles_per_split)
     fa_strerror(code), fa_tile_shape(B, Hq, M, D), fa_tile_counts(...), fa_schedule(...)
 
@@ -27,6 +29,11 @@ FA_F16, FA_BF16 = 0, 1
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, -1, -2, -3
 
 _lib = None
+
+
+class fa_strides(ctypes.Structure):
+    """Element strides of the batch, head and row axes of a [B, H, S, D] tensor (D has unit stride)."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
 
 
 class FaError(RuntimeError):
@@ -60,6 +67,12 @@ def _load():
     lib.fa_splitkv_plan.restype = ci
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, ci, vp, sz, vp]
     lib.fa_fwd_splitkv.restype = ci
+    sp = ctypes.POINTER(fa_strides)
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, sp, sp, sp, sp, cf, ci, ci, vp]
+    lib.fa_fwd_strided.restype = ci
+    lib.fa_fwd_splitkv_strided.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, sp, sp, sp, sp, cf, ci, ci, ci,
+                                           vp, sz, vp]
+    lib.fa_fwd_splitkv_strided.restype = ci
     _lib = lib
     return lib
 
@@ -74,6 +87,30 @@ def library():
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream) -> int:
     """Raw C ABI call: pointers are integers (device addresses), stream an int or None."""
     return _load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, M, N, D, float(scale), int(causal), int(dtype), stream)
+
+
+def _st(x):
+    """None -> NULL; a (batch, head, row) triple or fa_strides -> pointer to fa_strides."""
+    if x is None:
+        return None
+    if not isinstance(x, fa_strides):
+        x = fa_strides(*[int(v) for v in x])
+    return ctypes.pointer(x)
+
+
+def fa_fwd_strided(q, k, v, o, lse, B, Hq, Hkv, M, N, D, q_strides, k_strides, v_strides, o_strides, scale, causal,
+                   dtype, stream) -> int:
+    """Raw C ABI call with element strides (batch, head, row) per tensor, None for contiguous."""
+    return _load().fa_fwd_strided(q, k, v, o, lse, B, Hq, Hkv, M, N, D, _st(q_strides), _st(k_strides),
+                                  _st(v_strides), _st(o_strides), float(scale), int(causal), int(dtype), stream)
+
+
+def fa_fwd_splitkv_strided(q, k, v, o, lse, B, Hq, Hkv, M, N, D, q_strides, k_strides, v_strides, o_strides, scale,
+                           causal, dtype, tiles_per_split, workspace, workspace_bytes, stream) -> int:
+    """Raw C ABI call of the strided key-split forward."""
+    return _load().fa_fwd_splitkv_strided(q, k, v, o, lse, B, Hq, Hkv, M, N, D, _st(q_strides), _st(k_strides),
+                                          _st(v_strides), _st(o_strides), float(scale), int(causal), int(dtype),
+                                          int(tiles_per_split), workspace, int(workspace_bytes), stream)
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, causal, dtype, tiles_per_split, workspace,
@@ -139,8 +176,10 @@ def _dtype_code(t) -> int:
 
 def attention_forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None,
                       split_kv="auto"):
-    """O, lse = softmax(mask(q k^T * scale)) v for contiguous device tensors
-    q [B,Hq,M,D], k/v [B,Hkv,N,D] (fp16 or bf16).  Returns (o [B,Hq,M,D], lse [B,Hq,M] fp32).
+    """O, lse = softmax(mask(q k^T * scale)) v for device tensors q [B,Hq,M,D], k/v [B,Hkv,N,D]
+    (fp16 or bf16) with unit stride along D and any other strides that keep rows 16-byte aligned
+    (e.g. [B,S,H,D] buffers passed as .transpose(1, 2) views).  Returns (o [B,Hq,M,D], lse
+    [B,Hq,M] fp32); a new `o` takes q's memory layout.
 
     split_kv: "auto" runs the key-split forward when its plan splits some query tile (small
     grids) or when M < 128 with grouped KV heads (the key-split kernel then stacks the query
@@ -153,10 +192,10 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D [B, H, S, D]")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have unit stride along D")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     B, Hq, M, D = q.shape
@@ -166,9 +205,15 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q)  # preserves q's layout when q is a permuted dense tensor
+    if out.stride(3) != 1 or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype, with unit stride along D")
     if lse is None:
         lse = torch.empty((B, Hq, M), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, M) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a contiguous float32 [B, Hq, M] tensor")
+    strided = not all(t.is_contiguous() for t in (q, k, v, out))
+    sts = [tuple(t.stride()[:3]) if strided else None for t in (q, k, v, out)]
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     if split_kv is not False:
@@ -180,19 +225,20 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
             _, _, ws_bytes = fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles)
             if ws_bytes > 0 or split_kv != "auto" or (M < 128 and Hq > Hkv):
                 ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-                rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
-                                    Hkv, M, N, D, scale, causal, _dtype_code(q), tiles, ws.data_ptr(), ws_bytes, stream)
+                rc = fa_fwd_splitkv_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                                            Hq, Hkv, M, N, D, *sts, scale, causal, _dtype_code(q), tiles,
+                                            ws.data_ptr(), ws_bytes, stream)
                 if rc != FA_OK:
                     raise FaError(rc, "fa_fwd_splitkv")
                 return out, lse
         elif split_kv != "auto":
             raise ValueError("the key-split forward needs D in (64, 128) and M <= 16384")
-    rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, M, N, D,
-                scale, causal, _dtype_code(q), stream)
+    rc = fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, M, N,
+                        D, *sts, scale, causal, _dtype_code(q), stream)
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd")
     return out, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_splitkv_plan", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+__all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]

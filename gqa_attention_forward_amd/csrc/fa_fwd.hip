@@ -121,6 +121,8 @@ struct Params {
     const void *q, *k, *v;
     void *o;
     float *lse;
+    // element strides of the batch, head and row axes (the head-dim axis has unit stride)
+    long long q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
     int B, Hq, Hkv, M, N;
     int n_qt;           // query tiles per (b, h)
     long long total;    // workgroups in the grid
@@ -215,8 +217,8 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     const int t0 = split * kr.n_tiles / n_split;
     const int n_tiles = (split + 1) * kr.n_tiles / n_split - t0;
 
-    const T *kg = (const T *)p.k + ((size_t)tc.b * p.Hkv + hk) * (size_t)N * D;
-    const T *vg = (const T *)p.v + ((size_t)tc.b * p.Hkv + hk) * (size_t)N * D;
+    const T *kg = (const T *)p.k + tc.b * p.k_sb + hk * p.k_sh;
+    const T *vg = (const T *)p.v + tc.b * p.v_sb + hk * p.v_sh;
 
     const int qrow = m0 + wave * 32 + ql;  // this lane's row of the unit
     const bool qvalid = qrow < R;
@@ -225,7 +227,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         qpos = qrow % M;
         qhead = tc.h + qrow / M;
     }
-    const T *qg = (const T *)p.q + (((size_t)tc.b * p.Hq + qhead) * (size_t)M + qpos) * D;  // read only if qvalid
+    const T *qg = (const T *)p.q + tc.b * p.q_sb + qhead * p.q_sh + qpos * p.q_ss;  // read only if qvalid
 
     // ---- A2: the Q operand, resident in registers (B operand of S^T = K Q^T)
     u32x4 qreg[KS];
@@ -249,36 +251,37 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     constexpr int LOADS_PER_TILE = KI + VI;  // per wave
     static_assert(LOADS_PER_TILE < 16, "wait count encoding");
     constexpr unsigned kPad = 0x7fffff00u;  // an offset past the end of every tile resource
-    constexpr int TILE_GBYTES = kBN * D * (int)sizeof(T);
     lds_u8 *const sink = smem + NBUF * (K_TILE + V_TILE);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    // loads of tiles past this workgroup's share (the pipeline runs ahead) read as zero
-    const long long kv_bytes_all = (long long)N * D * (long long)sizeof(T);
-    const long long kv_bytes = (long long)(t0 + n_tiles) * TILE_GBYTES < kv_bytes_all
-                                   ? (long long)(t0 + n_tiles) * TILE_GBYTES : kv_bytes_all;
+    // key rows at or past kv_end read as zero: the end of the keys, or of this workgroup's share
+    // (the pipeline's look-ahead loads run past it)
+    const int kv_end = (t0 + n_tiles) * kBN < N ? (t0 + n_tiles) * kBN : N;
+    const int k_rs = (int)(p.k_ss * (long long)sizeof(T)), v_rs = (int)(p.v_ss * (long long)sizeof(T));  // row bytes
     unsigned k_src[KI], v_src[VI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
         const int u = (wave_u + kWaves * i) * 64 + lane;  // 16-byte unit of the K tile this lane fills
         const int slot = u / (KP / 16), unit = u % (KP / 16);
         const int key = (slot & ~31) | pi32(slot & 31);    // slot order pi inside each 32-key block
-        k_src[i] = unit < UNITS && u < K_INSTR * 64 ? (unsigned)(key * D * (int)sizeof(T) + unit * 16) : kPad;
+        k_src[i] = unit < UNITS && u < K_INSTR * 64 ? (unsigned)(key * k_rs + unit * 16) : kPad;
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
         const int u = (wave_u + kWaves * i) * 64 + lane;
         const int row = u / (VP / 16), unit = u % (VP / 16);
-        v_src[i] = unit < UNITS && u < V_INSTR * 64 ? (unsigned)(row * D * (int)sizeof(T) + unit * 16) : kPad;
+        v_src[i] = unit < UNITS && u < V_INSTR * 64 ? (unsigned)(row * v_rs + unit * 16) : kPad;
     }
-    auto tile_rsrc = [&](const T *base, int t) {
-        const long long off = (long long)t * TILE_GBYTES;
-        const long long rem = kv_bytes - off;
-        return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + off), (short)0,
-                                                 (int)(rem > 0 ? (rem < TILE_GBYTES ? rem : TILE_GBYTES) : 0),
-                                                 0x00020000);
+    // buffer resource of key tile t: its rows up to kv_end, so a row past it (every byte of which
+    // lies at or beyond (rows - 1) * row_bytes + D * sizeof(T)) reads as zero
+    auto tile_rsrc = [&](const T *base, int row_bytes, int t) {
+        const int r0 = t * kBN;
+        const int rows = kv_end - r0 < kBN ? kv_end - r0 : kBN;
+        const int bytes = rows > 0 ? (rows - 1) * row_bytes + D * (int)sizeof(T) : 0;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + (long long)r0 * row_bytes), (short)0,
+                                                 bytes, 0x00020000);
     };
     auto load_k = [&](int t, int buf) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, t0 + t);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, k_rs, t0 + t);
         lds_u8 *dst = smem + buf * K_TILE;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
@@ -287,7 +290,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         }
     };
     auto load_v = [&](int t, int buf) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, t0 + t);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, v_rs, t0 + t);
         lds_u8 *dst = smem + NBUF * K_TILE + buf * V_TILE;
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
@@ -583,7 +586,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
                 if (hh == 0) p.ws_lse[slot] = lse;
             }
         } else {
-            T *og = (T *)p.o + row * D;
+            T *og = (T *)p.o + tc.b * p.o_sb + qhead * p.o_sh + qpos * p.o_ss;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 u32x4 w0, w1;
@@ -652,7 +655,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(SplitParams p)
     u32x2 w;
     w[0] = Elem<T>::pack2(acc[0] * inv, acc[1] * inv);
     w[1] = Elem<T>::pack2(acc[2] * inv, acc[3] * inv);
-    *(u32x2 *)((T *)p.o + row * D + col) = w;
+    *(u32x2 *)((T *)p.o + b * p.o_sb + h * p.o_sh + i * p.o_ss + col) = w;
     if (col == 0) p.lse[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
@@ -695,6 +698,8 @@ static hipError_t launch_t(const Params &p, int D, int W, bool causal, hipStream
 // ---- key-split mode (4-wave workgroups, 128-row query tiles)
 
 constexpr int kSplitBM = 128;
+// largest K/V row stride (elements): a key tile's 32-bit buffer range must hold 63 rows plus one
+constexpr long long kMaxKvRowStride = ((0x7fff0000LL / 2) - 128) / 63;
 constexpr int kSplitTargetWgs = 512;  // two 4-wave workgroups per CU
 constexpr int kSplitMinTiles = 8;     // smallest share the automatic plan hands one workgroup
 constexpr int kSplitMinRange = 32;    // the automatic plan splits only query tiles this long or longer
@@ -785,9 +790,34 @@ static hipError_t launch_split(const SplitParams &p, int D, bool causal, hipStre
     return D == 128 ? launch_split_d<T, 128>(p, causal, stream) : launch_split_d<T, 64>(p, causal, stream);
 }
 
-// argument checks shared by the entry points; fills the sizes of p
+// Strides (in elements) of one [B, H, S, D] tensor: the caller's, or the contiguous ones for
+// NULL.  Every row must start 16-byte aligned (strides multiples of 8 elements), strides are
+// non-negative, and the largest element offset must fit in int64.  K and V rows are addressed
+// with 32-bit offsets inside one key tile, which bounds their row stride.
+static int strides_of(const fa_strides *st, int B, int H, int S, int D, bool kv, long long *sb, long long *sh,
+                      long long *ss)
+{
+    if (!st) {
+        *ss = D;
+        *sh = (long long)S * D;
+        *sb = (long long)H * S * D;
+        return FA_OK;
+    }
+    if (st->batch < 0 || st->head < 0 || st->row < 0) return FA_ERR_INVALID_ARG;
+    if ((st->batch | st->head | st->row) & 7) return FA_ERR_UNSUPPORTED;
+    const double last = (double)(B - 1) * st->batch + (double)(H - 1) * st->head + (double)(S - 1) * st->row + D;
+    if (last > 9.0e18) return FA_ERR_INVALID_ARG;
+    if (kv && st->row > kMaxKvRowStride) return FA_ERR_UNSUPPORTED;
+    *sb = st->batch;
+    *sh = st->head;
+    *ss = st->row;
+    return FA_OK;
+}
+
+// argument checks shared by the entry points; fills the sizes and strides of p
 static int check_args(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
-                      int N, int D, float scale, int dtype, Params *p)
+                      int N, int D, const fa_strides *qs, const fa_strides *ks, const fa_strides *vs,
+                      const fa_strides *os, float scale, int dtype, Params *p)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 || D <= 0) return FA_ERR_INVALID_ARG;
@@ -798,8 +828,11 @@ static int check_args(const void *q, const void *k, const void *v, void *o, floa
     const double nq = (double)B * Hq * M * D, nk = (double)B * Hkv * N * D;
     if (nq > 9.0e18 || nk > 9.0e18) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-    // K and V of one (b, kv head) are addressed with 32-bit buffer offsets
-    if ((long long)N * D * 2 > 0x7fff0000LL) return FA_ERR_UNSUPPORTED;
+    int rc;
+    if ((rc = strides_of(qs, B, Hq, M, D, false, &p->q_sb, &p->q_sh, &p->q_ss)) != FA_OK) return rc;
+    if ((rc = strides_of(ks, B, Hkv, N, D, true, &p->k_sb, &p->k_sh, &p->k_ss)) != FA_OK) return rc;
+    if ((rc = strides_of(vs, B, Hkv, N, D, true, &p->v_sb, &p->v_sh, &p->v_ss)) != FA_OK) return rc;
+    if ((rc = strides_of(os, B, Hq, M, D, false, &p->o_sb, &p->o_sh, &p->o_ss)) != FA_OK) return rc;
     const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
     if (align & 15u) return FA_ERR_UNSUPPORTED;
     p->q = q;
@@ -869,11 +902,14 @@ int fa_schedule(int B, int Hq, int Hkv, int M, int D, int causal, long long wg, 
     return FA_OK;
 }
 
-int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M, int N,
-           int D, float scale, int causal, int dtype, void *stream)
+int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
+                   int N, int D, const fa_strides *q_strides, const fa_strides *k_strides,
+                   const fa_strides *v_strides, const fa_strides *o_strides, float scale, int causal, int dtype,
+                   void *stream)
 {
     fa::Params p;
-    int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, dtype, &p);
+    int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, q_strides, k_strides, v_strides, o_strides, scale,
+                            dtype, &p);
     if (rc != FA_OK) return rc;
     int BM, BN;
     if (fa::tile_shape(B, Hq, M, D, &BM, &BN) != FA_OK) return FA_ERR_UNSUPPORTED;
@@ -886,6 +922,13 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     hipError_t err = dtype == FA_F16 ? fa::launch_t<_Float16>(p, D, W, causal != 0, s)
                                      : fa::launch_t<__bf16>(p, D, W, causal != 0, s);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M, int N,
+           int D, float scale, int causal, int dtype, void *stream)
+{
+    return fa_fwd_strided(q, k, v, o, lse, B, Hq, Hkv, M, N, D, nullptr, nullptr, nullptr, nullptr, scale, causal,
+                          dtype, stream);
 }
 
 int fa_splitkv_plan(int B, int Hq, int Hkv, int M, int N, int D, int causal, int tiles_per_split, int *tiles_used,
@@ -903,12 +946,14 @@ int fa_splitkv_plan(int B, int Hq, int Hkv, int M, int N, int D, int causal, int
     return FA_OK;
 }
 
-int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
-                   int N, int D, float scale, int causal, int dtype, int tiles_per_split, void *workspace,
-                   size_t workspace_bytes, void *stream)
+int fa_fwd_splitkv_strided(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
+                           int M, int N, int D, const fa_strides *q_strides, const fa_strides *k_strides,
+                           const fa_strides *v_strides, const fa_strides *o_strides, float scale, int causal,
+                           int dtype, int tiles_per_split, void *workspace, size_t workspace_bytes, void *stream)
 {
     fa::SplitPlan pl;
-    int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, dtype, &pl.sp);
+    int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, q_strides, k_strides, v_strides, o_strides, scale,
+                            dtype, &pl.sp);
     if (rc != FA_OK) return rc;
     rc = fa::split_plan(B, Hq, Hkv, M, N, D, causal != 0, tiles_per_split, &pl);
     if (rc != FA_OK) return rc;
@@ -926,6 +971,14 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
     hipError_t err = dtype == FA_F16 ? fa::launch_split<_Float16>(pl.sp, D, causal != 0, s)
                                      : fa::launch_split<__bf16>(pl.sp, D, causal != 0, s);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
+                   int N, int D, float scale, int causal, int dtype, int tiles_per_split, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    return fa_fwd_splitkv_strided(q, k, v, o, lse, B, Hq, Hkv, M, N, D, nullptr, nullptr, nullptr, nullptr, scale,
+                                  causal, dtype, tiles_per_split, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

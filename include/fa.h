@@ -40,13 +40,20 @@ extern "C" {
 /* input/output element type */
 typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
+/* Element strides of the batch, head and row axes of a [B, H, S, D] tensor; the D axis always
+ * has unit stride.  Contiguous row-major is {H*S*D, S*D, D}; a [B, S, H, D] buffer viewed as
+ * [B, H, S, D] is {S*H*D, D, H*D}. */
+typedef struct {
+    long long batch, head, row;
+} fa_strides;
+
 /* return codes */
 enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, Hq % Hkv != 0, scale not finite or <= 0,
                                 unknown dtype, sizes whose element counts overflow int64 */
-    FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, a pointer not 16-byte aligned, one KV head's K (or V)
-                                larger than 2 GiB, or a grid beyond 2^31 - 1 workgroups */
+    FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, a pointer or row not 16-byte aligned, a K/V row stride
+                                over 17 043 456 elements, or a grid beyond 2^31 - 1 workgroups */
     FA_ERR_LAUNCH = -3       /* the kernel launch reported an error (hipGetLastError) */
 };
 
@@ -66,7 +73,8 @@ enum {
  *   dtype                FA_F16 or FA_BF16
  *   stream               a hipStream_t, or NULL for the default stream
  *
- * All pointers must be 16-byte aligned.  Indexing is 64-bit.
+ * All pointers must be 16-byte aligned.  Indexing is 64-bit (K and V rows inside one 64-key tile
+ * use 32-bit buffer offsets).
  *
  * Behaviour: validates every argument before any HIP call and returns a negative code
  * without touching the GPU if one is bad.  Otherwise enqueues one kernel on `stream`
@@ -77,6 +85,23 @@ enum {
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M, int N,
            int D, float scale, int causal, int dtype, void *stream);
+
+/*
+ * fa_fwd_strided -- fa_fwd on tensors with arbitrary batch / head / row strides ("从零开始写Qwen3"
+ * (derivation article), section "FlashAttention": the kernel listing takes a stride for every
+ * axis of q, k, v and o).  A NULL stride pointer means that tensor is contiguous, so
+ * fa_fwd(...) == fa_fwd_strided(..., NULL, NULL, NULL, NULL, ...).  lse stays contiguous
+ * [B, Hq, M].  Strides must be non-negative multiples of 8 elements (every row 16-byte aligned);
+ * zero strides may broadcast q, k or v, but o's rows must not overlap each other or q, k, v.
+ * K and V row strides are at most 17 043 456 elements.  Results are bitwise those of fa_fwd on
+ * the same values stored contiguously.  Errors as fa_fwd (FA_ERR_INVALID_ARG for a negative
+ * stride or offsets past int64, FA_ERR_UNSUPPORTED for a stride not a multiple of 8 or a K/V row
+ * stride over the limit).
+ */
+int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
+                   int N, int D, const fa_strides *q_strides, const fa_strides *k_strides,
+                   const fa_strides *v_strides, const fa_strides *o_strides, float scale, int causal, int dtype,
+                   void *stream);
 
 /* Human-readable text for a return code (static storage; never NULL). */
 const char *fa_strerror(int code);
@@ -122,6 +147,11 @@ int fa_splitkv_plan(int B, int Hq, int Hkv, int M, int N, int D, int causal, int
 int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
                    int N, int D, float scale, int causal, int dtype, int tiles_per_split, void *workspace,
                    size_t workspace_bytes, void *stream);
+/* fa_fwd_splitkv on strided tensors (strides as for fa_fwd_strided; NULL = contiguous). */
+int fa_fwd_splitkv_strided(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
+                           int M, int N, int D, const fa_strides *q_strides, const fa_strides *k_strides,
+                           const fa_strides *v_strides, const fa_strides *o_strides, float scale, int causal,
+                           int dtype, int tiles_per_split, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Introspection of the launch plan (host-only, no GPU needed).  These report the tiling

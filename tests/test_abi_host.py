@@ -143,3 +143,31 @@ def test_splitkv_plan_invalid():
         fa.fa_splitkv_plan(1, 3, 2, 16, 16, 64, True)
     with pytest.raises(fa.FaError):
         fa.fa_splitkv_plan(1, 2, 1, 16385, 16, 64, True)
+
+
+# ------------------------------------------------------------ strided entry points
+
+def _call_strided(qs=None, ks=None, vs=None, os_=None, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["M"], a["N"],
+                             a["D"], qs, ks, vs, os_, a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("bad", [dict(qs=(-64, 1024, 64)), dict(ks=(0, -8, 64)), dict(os_=(1024, 64, -64)),
+                                 dict(B=0, qs=(1024, 512, 64))])
+def test_strided_invalid(bad):
+    assert _call_strided(**bad) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(qs=(2048, 1024, 68)), dict(vs=(2048, 1028, 64)), dict(os_=(2052, 1024, 64)),
+                                 dict(ks=(1 << 40, 1 << 30, 1 << 25)), dict(D=96, ks=(4096, 2048, 128))])
+def test_strided_unsupported(bad):
+    assert _call_strided(**bad) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_strided_split_invalid():
+    st = fa.fa_strides(-8, 0, 64)
+    rc = fa.fa_fwd_splitkv_strided(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 1, 2, 1, 16, 16, 64, None, st, None, None,
+                                   0.125, 1, 0, 1, None, 0, None)
+    assert rc == fa.FA_ERR_INVALID_ARG
