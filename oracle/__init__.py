@@ -18,7 +18,9 @@ header states what is computed and which page passages each mode follows:
   denominator, rescaled accumulator, one division after the loop), in fp64;
 * ``attn_fwd_stepnorm``   -- the page's per-step-normalised online-softmax recurrence
   (section "在线softmax"), in fp64;
-* ``attn_probs``          -- the softmax weight matrix of one (b, h).
+* ``attn_probs``          -- the softmax weight matrix of one (b, h);
+* ``attn_bwd``            -- gradients of O with respect to q, k, v for an upstream dO,
+  the chain rule of the definition written out (not on the pages; see the C file).
 
 Every function is pinned by the ``-m "not gpu"`` tests against closed forms, page
 worked numbers, invariants and an independent library routine.
@@ -52,6 +54,8 @@ def _load():
         lib.oracle_attn_fwd_blockwise.argtypes = [u16p, u16p, u16p] + shape + [cl, dp, dp]
         lib.oracle_attn_fwd_stepnorm.argtypes = [u16p, u16p, u16p] + shape + [cl, dp, dp]
         lib.oracle_attn_probs.argtypes = [u16p, u16p] + shape + [ci, ci, dp]
+        lib.oracle_attn_bwd.argtypes = [u16p, u16p, u16p, u16p] + shape + [dp, dp, dp]
+        lib.oracle_attn_bwd.restype = ci
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_f16.restype = cd
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
@@ -165,6 +169,23 @@ def attn_probs(q, k, scale: float, causal: bool, b: int, h: int, dtype: int | No
     if rc != 0:
         raise ValueError("oracle_attn_probs rejected its arguments")
     return P
+
+
+def attn_bwd(q, k, v, do, scale: float, causal: bool, dtype: int | None = None):
+    """Gradients (dq [B,Hq,M,D], dk [B,Hkv,N,D], dv [B,Hkv,N,D]) fp64 of O for upstream dO."""
+    dtype, (B, Hq, Hkv, M, N, D), qb, kb, vb = _common(q, k, v, dtype)
+    dob = _bits(do)
+    assert dob.shape == qb.shape
+    dq = np.empty((B, Hq, M, D), np.float64)
+    dk = np.empty((B, Hkv, N, D), np.float64)
+    dv = np.empty((B, Hkv, N, D), np.float64)
+    rc = _load().oracle_attn_bwd(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
+                                 _ptr(dob, ctypes.c_uint16), dtype, B, Hq, Hkv, M, N, D, float(scale),
+                                 int(bool(causal)), _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                                 _ptr(dv, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dv
 
 
 def decode(bits: int, dtype: int) -> float:

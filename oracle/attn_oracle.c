@@ -408,3 +408,127 @@ int oracle_attn_probs(const uint16_t *q16, const uint16_t *k16, int dtype, int B
     free(k);
     return 0;
 }
+
+/* ------------------------------------------------------------------ backward */
+
+/*
+ * Gradients of O with respect to q, k and v for an upstream gradient dO (same shape as O),
+ * written out from the chain rule of the definition above (not on the pages; lse is a saved
+ * statistic of the forward and is not differentiated).  With z_ij = scale * q_i . k_j the
+ * logits of row i over its visible keys and P_ij = softmax_j(z_ij):
+ *
+ *   O_i   = sum_j P_ij v_j                       -> dv_j  += P_ij dO_i
+ *                                                   dP_ij  = dO_i . v_j
+ *   P_i.  = softmax(z_i.)   (Jacobian diag(P) - P P^T)
+ *                                                -> dz_ij  = P_ij (dP_ij - sum_k P_ik dP_ik)
+ *   z_ij  = scale q_i . k_j                      -> dq_i  += scale dz_ij k_j
+ *                                                   dk_j  += scale dz_ij q_i
+ *
+ * A KV head's dk and dv sum the contributions of every query head that reads it (the
+ * grouped mapping h -> h / (Hq / Hkv)).  A row with no visible key contributes nothing and
+ * gets dq = 0.  Outputs are fp64, contiguous: dq [B,Hq,M,D], dk and dv [B,Hkv,N,D].
+ * Parallel over (b, kv head): each thread owns the dk/dv of its KV head.
+ */
+int oracle_attn_bwd(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16, const uint16_t *do16, int dtype,
+                    int B, int Hq, int Hkv, int M, int N, int D, double scale, int causal, double *dq, double *dk,
+                    double *dv)
+{
+    if (!q16 || !k16 || !v16 || !do16 || !dq || !dk || !dv || B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 ||
+        D <= 0)
+        return -1;
+    if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1))
+        return -1;
+    size_t nq = (size_t)B * Hq * M * D, nk = (size_t)B * Hkv * N * D;
+    problem p;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.M = M;
+    p.N = N;
+    p.D = D;
+    p.causal = causal;
+    p.scale = scale;
+    double *q = decode_all(q16, nq, dtype), *k = decode_all(k16, nk, dtype), *v = decode_all(v16, nk, dtype);
+    double *dO = decode_all(do16, nq, dtype);
+    if (!q || !k || !v || !dO) {
+        free(q);
+        free(k);
+        free(v);
+        free(dO);
+        return -1;
+    }
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    memset(dq, 0, nq * sizeof(double));
+    memset(dk, 0, nk * sizeof(double));
+    memset(dv, 0, nk * sizeof(double));
+    const int g = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *z = (double *)malloc((size_t)N * sizeof(double));
+        double *P = (double *)malloc((size_t)N * sizeof(double));
+        double *dP = (double *)malloc((size_t)N * sizeof(double));
+        if (!z || !P || !dP) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int bhk = 0; bhk < B * Hkv; ++bhk) {
+                int b = bhk / Hkv, hk = bhk % Hkv;
+                for (int h = hk * g; h < (hk + 1) * g; ++h) {
+                    for (long i = 0; i < M; ++i) {
+                        long nv = visible_count(&p, i);
+                        if (nv == 0)
+                            continue;
+                        const double *qi = q_row(&p, b, h, i);
+                        const double *doi = dO + (((size_t)b * Hq + h) * M + i) * D;
+                        /* P_i. = softmax over the visible keys */
+                        double m = -INFINITY;
+                        for (long j = 0; j < nv; ++j) {
+                            z[j] = score(&p, qi, k_row(&p, b, hk, j));
+                            if (z[j] > m)
+                                m = z[j];
+                        }
+                        double l = 0.0;
+                        for (long j = 0; j < nv; ++j)
+                            l += exp(z[j] - m);
+                        for (long j = 0; j < nv; ++j)
+                            P[j] = exp(z[j] - m) / l;
+                        /* dP_ij = dO_i . v_j and its P-weighted mean */
+                        double mean = 0.0;
+                        for (long j = 0; j < nv; ++j) {
+                            const double *vj = v_row(&p, b, hk, j);
+                            double acc = 0.0;
+                            for (int d = 0; d < D; ++d)
+                                acc += doi[d] * vj[d];
+                            dP[j] = acc;
+                            mean += P[j] * acc;
+                        }
+                        double *dqi = dq + (((size_t)b * Hq + h) * M + i) * D;
+                        for (long j = 0; j < nv; ++j) {
+                            double dz = P[j] * (dP[j] - mean);
+                            const double *kj = k_row(&p, b, hk, j);
+                            double *dkj = dk + (((size_t)b * Hkv + hk) * N + j) * D;
+                            double *dvj = dv + (((size_t)b * Hkv + hk) * N + j) * D;
+                            for (int d = 0; d < D; ++d) {
+                                dqi[d] += scale * dz * kj[d];
+                                dkj[d] += scale * dz * qi[d];
+                                dvj[d] += P[j] * doi[d];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(z);
+        free(P);
+        free(dP);
+    }
+    free(q);
+    free(k);
+    free(v);
+    free(dO);
+    return err ? -1 : 0;
+}
