@@ -50,6 +50,8 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward, or the backward (dq, dk, dv from a forward's O and lse)")
     ap.add_argument("--layout", choices=["bhsd", "bshd"], default="bhsd",
                     help="memory layout of q, k, v, o: contiguous [B,H,S,D] or [B,S,H,D] buffers (strided path)")
     ap.add_argument("--split-kv", default="auto",
@@ -109,6 +111,31 @@ def time_gpu(fa, w, q, k, v, steps, warmup, split_kv="auto"):
     wall = time.perf_counter() - t0
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
     return wall, durs, o, lse
+
+
+def time_gpu_bwd(fa, w, q, k, v, steps, warmup):
+    """Backward calls on fixed q, k, v, dO and the forward's O and lse (per-call HIP events)."""
+    import torch
+
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 1000)
+    do = torch.randn(q.shape, generator=g).to(w.dtype).to(q.device)
+    q, k, v = (t.contiguous() for t in (q, k, v))
+    o, lse = fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, split_kv=False)
+    for _ in range(warmup):
+        fa.attention_backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        grads = fa.attention_backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
+    return wall, durs, grads[0], lse
 
 
 def cpu_baseline(w, q, k, v, target_s):
@@ -202,22 +229,27 @@ def main():
         if args.layout == "bshd":  # the same values in [B, S, H, D] buffers, passed as [B, H, S, D] views
             q, k, v = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
         torch.cuda.synchronize()
-        wall, durs, o, lse = time_gpu(fa, w, q, k, v, args.steps, args.warmup, split_kv)
+        if args.which == "bwd":
+            wall, durs, o, lse = time_gpu_bwd(fa, w, q, k, v, args.steps, args.warmup)
+        else:
+            wall, durs, o, lse = time_gpu(fa, w, q, k, v, args.steps, args.warmup, split_kv)
         path = "fa_fwd"
         if split_kv is not False and w.M <= 16384:
             tiles, wgs, ws = fa.fa_splitkv_plan(w.B, w.Hq, w.Hkv, w.M, w.N, w.D, w.causal,
                                                 0 if split_kv == "auto" else split_kv)
-            if ws > 0 or split_kv != "auto":
+            if args.which == "fwd" and (ws > 0 or split_kv != "auto"):
                 path = f"fa_fwd_splitkv ({tiles} key tiles a share, {wgs} workgroups, merge)"
-        flops = accounting.workload_flops(w)
+        # backward: five products per visible pair (S, dP, dV, dK, dQ) against the forward's two
+        flops = accounting.workload_flops(w) * (2.5 if args.which == "bwd" else 1.0)
         tflops = flops * args.steps / wall / 1e12
         avg_ms = sum(durs) / len(durs)
         achieved = flops / (avg_ms * 1e-3) / 1e12
         bm, bn = fa.fa_tile_shape(w.B, w.Hq, w.M, w.D)
         f_, m_, _ = fa.fa_tile_counts(w.M, w.N, bm, bn, w.causal)
-        issued = 4 * bm * bn * w.D * (f_ + m_) * w.B * w.Hq
+        issued = 4 * bm * bn * w.D * (f_ + m_) * w.B * w.Hq * (2.5 if args.which == "bwd" else 1.0)
         line = {
-            "workload": name, "layout": args.layout, "path": path, "tflops": round(tflops, 2), "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "workload": name, "pass": args.which, "layout": args.layout,
+            "path": "fa_bwd (prep, dq, dk/dv)" if args.which == "bwd" else path, "tflops": round(tflops, 2), "kernel_avg_us": round(avg_ms * 1e3, 2),
             "kernel_median_us": round(durs[len(durs) // 2] * 1e3, 2), "kernel_min_us": round(durs[0] * 1e3, 2),
             "pct_mfma_peak": round(100 * achieved / MFMA_PEAK_TFLOPS, 2),
             "issued_mfma_tflops": round(issued / (avg_ms * 1e-3) / 1e12, 2),
@@ -226,9 +258,11 @@ def main():
         print(json.dumps(line), file=sys.stderr, flush=True)
         if name == args.workload:
             assert torch.isfinite(o.float()).all().item(), "non-finite output"
-            traffic = read_traffic(name)
+            traffic = read_traffic(name) if args.which == "fwd" else None
             result = {
-                "metric": "attention fwd TFLOPS (causal-adjusted) and % of MI355X FP16/BF16 MFMA peak",
+                "metric": ("attention fwd TFLOPS (causal-adjusted) and % of MI355X FP16/BF16 MFMA peak"
+                           if args.which == "fwd" else
+                           "attention bwd TFLOPS (causal-adjusted, 2.5x forward flops) and % of MI355X FP16/BF16 MFMA peak"),
                 "value": round(tflops, 3),
                 "unit": "TFLOPS",
                 "n_gpus": 1,
@@ -240,14 +274,14 @@ def main():
                 "vs_baseline": None,
                 "dtype": "bf16" if w.dtype == torch.bfloat16 else "f16",
                 "data": "synthetic",
-                "config": {"workload": name, "layout": args.layout, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "M": w.M, "N": w.N, "D": w.D,
+                "config": {"workload": name, "pass": args.which, "layout": args.layout, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "M": w.M, "N": w.N, "D": w.D,
                            "causal": w.causal, "seed": w.seed, "peaky_k_rows": w.peak_rate,
                            "parallelism": "single GPU"},
                 "pct_of_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 3),
                 "roofline": roofline(w, flops, avg_ms, traffic),
                 "cpu_baseline": None,
             }
-            if not args.no_cpu_baseline:
+            if not args.no_cpu_baseline and args.which == "fwd":
                 result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
         del q, k, v, o, lse
         torch.cuda.empty_cache()

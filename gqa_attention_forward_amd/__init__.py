@@ -73,6 +73,10 @@ def _load():
     lib.fa_fwd_splitkv_strided.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, sp, sp, sp, sp, cf, ci, ci, ci,
                                            vp, sz, vp]
     lib.fa_fwd_splitkv_strided.restype = ci
+    lib.fa_bwd_workspace_size.argtypes = [ci, ci, ci]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, sz, vp]
+    lib.fa_bwd.restype = ci
     _lib = lib
     return lib
 
@@ -128,6 +132,17 @@ def fa_splitkv_plan(B: int, Hq: int, Hkv: int, M: int, N: int, D: int, causal: b
     if rc != FA_OK:
         raise FaError(rc, "fa_splitkv_plan")
     return t.value, wg.value, ws.value
+
+
+def fa_bwd_workspace_size(B: int, Hq: int, M: int) -> int:
+    return int(_load().fa_bwd_workspace_size(B, Hq, M))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, M, N, D, scale, causal, dtype, workspace, workspace_bytes,
+           stream) -> int:
+    """Raw C ABI call of the backward pass (pointers as integers)."""
+    return _load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, M, N, D, float(scale), int(causal),
+                          int(dtype), workspace, int(workspace_bytes), stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -240,5 +255,35 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, stream=None):
+    """dq, dk, dv for contiguous device tensors: q, dout, o [B,Hq,M,D], k, v [B,Hkv,N,D] (fp16/bf16)
+    and lse [B,Hq,M] fp32 from attention_forward on the same inputs.  The workspace comes from
+    torch's caching allocator; kernels are enqueued on `stream` (default: the current stream)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, Hq, M, D = q.shape
+    _, Hkv, N, _ = k.shape
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch")
+    if tuple(lse.shape) != (B, Hq, M) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, M]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa_bwd_workspace_size(B, Hq, M)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, M, N, D, scale, causal, _dtype_code(q), ws.data_ptr(),
+                ws_bytes, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+__all__ = ["fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]

@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library libfa.so in-tree with hipcc.
 
-The library holds the fused attention forward kernels and their C ABI (include/fa.h).
+The library holds the fused attention forward and backward kernels and their C ABI (include/fa.h).
 """
 import os
 import shutil
@@ -9,7 +9,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip")]
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 
@@ -36,7 +36,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Always recompiles; returns the library path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + [SRC, "-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + SRCS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -103,6 +103,34 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
                    const fa_strides *v_strides, const fa_strides *o_strides, float scale, int causal, int dtype,
                    void *stream);
 
+/*
+ * fa_bwd -- backward pass: gradients of O with respect to q, k and v on one GPU.
+ *
+ * Not on the pages (they treat the forward only); the chain rule of the definition above, with
+ * P recomputed from the forward's lse and the softmax Jacobian's row term taken as
+ * Delta_i = dO_i . O_i (equal to sum_j P_ij dP_ij):
+ *     dv_j  = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . v_j - Delta_i),
+ *     dq_i  = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+ * where dk and dv of a KV head sum over the Hq / Hkv query heads that read it.  lse is not
+ * differentiated.
+ *
+ * Arguments (contiguous row-major DEVICE tensors owned by the caller, dtype as for fa_fwd):
+ *   q, k, v       the forward's inputs
+ *   o, lse        the forward's outputs (fa_fwd's O and lse for the same q, k, v, scale, causal)
+ *   dout          [B, Hq, M, D] upstream gradient of O
+ *   dq            [B, Hq, M, D] written;  dk, dv [B, Hkv, N, D] written (rounded to dtype)
+ *   workspace     at least fa_bwd_workspace_size(B, Hq, M) bytes of device memory, 16-byte
+ *                 aligned; overwritten (per-row Delta and lse statistics)
+ * Every pointer 16-byte aligned; outputs must not alias inputs.  Enqueues three kernels on
+ * `stream` and returns without synchronising; allocates nothing.  Rows that see no key get
+ * dq = 0; keys no row sees get dk = dv = 0.  Deterministic (no atomics).  Errors as fa_fwd,
+ * plus FA_ERR_INVALID_ARG for a missing or too small workspace.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int M);
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse, void *dq,
+           void *dk, void *dv, int B, int Hq, int Hkv, int M, int N, int D, float scale, int causal, int dtype,
+           void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable text for a return code (static storage; never NULL). */
 const char *fa_strerror(int code);
 
