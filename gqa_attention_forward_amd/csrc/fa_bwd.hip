@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
 // ------------------------------------------------------------------ dK/dV
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(Params p)
+__global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
 {
     constexpr int KS = D / 16, DB = D / 32, TILE = kTile * 2 * D;
     constexpr int BUF = 2 * TILE + 1024;  // Q tile, dO tile, stats chunk (512 bytes used)
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(Params p)
         const bool masked = n0 + kRows > N || i0 + kTile > M || (CAUSAL && i0 < diag);  // uniform
         const lds_u8 *qtile = smem + buf * BUF, *dtile = qtile + TILE;
         const float *stl = (const float *)(qtile + 2 * TILE);
-#pragma unroll
+#pragma unroll 1
         for (int qb = 0; qb < 2; ++qb) {
             f32x16 s, dp;
 #pragma unroll
@@ -391,8 +391,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(Params p)
                 s = Elem<T>::mfma(read_row<D>(qtile, qb * 32 + kl, 2 * ks + hh), kreg[ks], s);
                 dp = Elem<T>::mfma(read_row<D>(dtile, qb * 32 + kl, 2 * ks + hh), vreg[ks], dp);
             }
-            // register r is query i0 + 32 qb + 8 (r/4) + 4 hh + r%4 of this lane's key
-            f32x16 pr, ds;
+            // register r is query i0 + 32 qb + 8 (r/4) + 4 hh + r%4 of this lane's key; P replaces
+            // S and dS replaces dP in place
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int qi = qb * 32 + 8 * gq + 4 * hh;
@@ -406,14 +406,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(Params p)
                         const int i = i0 + qi + e;
                         x = kvalid && i < M && (!CAUSAL || key <= i + (N - M)) ? x : 0.f;
                     }
-                    pr[r] = x;
-                    ds[r] = x * (dp[r] - d4[e]);
+                    s[r] = x;
+                    dp[r] = x * (dp[r] - d4[e]);
                 }
             }
             // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const u32x4 bp = pack_b<T>(pr, tt), bs = pack_b<T>(ds, tt);
+                const u32x4 bp = pack_b<T>(s, tt), bs = pack_b<T>(dp, tt);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dv[db] = Elem<T>::mfma(read_tr<D>(dtile, tro, qb * 32 + 16 * tt, db), bp, dv[db]);
