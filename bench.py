@@ -36,7 +36,8 @@ if ROOT not in sys.path:
 
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "gqa_attention_forward_amd", "csrc", "fa_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "gqa_attention_forward_amd", "csrc", f)
+               for f in ("fa_fwd.hip", "fa_device.h", "fa_tiles.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_long_causal_gqa_16k_traffic.md")
 
 
@@ -60,8 +61,13 @@ def _parse():
 
 
 def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the forward kernel's sources (fa_fwd.hip, then the
+    headers it includes from csrc/, in that order)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str):
