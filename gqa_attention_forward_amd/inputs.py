@@ -85,3 +85,65 @@ def make_custom(B, Hq, Hkv, M, N, D, dtype, seed, *, peak_rate=0.0, device="cpu"
     """Inputs for an arbitrary shape with the same recipe (parity tests, ragged cases)."""
     w = Workload("custom", B, Hq, Hkv, M, N, D, dtype, False, seed, peak_rate=peak_rate)
     return make_inputs(w, device)[:3]
+
+
+# ------------------------------------------------------------ Gated DeltaNet prefill inputs
+
+@dataclasses.dataclass(frozen=True)
+class GdnWorkload:
+    """Chunked Gated DeltaNet prefill: q, k [B,T,Hqk,DK]; v [B,T,Hv,DV]; per value head and token
+    the gate's cumulative log inside each 64-token chunk (g) and beta; optional fp32 initial
+    state [B,Hv,DK,DV]."""
+    name: str
+    B: int
+    T: int
+    Hqk: int
+    Hv: int
+    DK: int
+    DV: int
+    dtype: torch.dtype
+    seed: int
+    init_state: bool = False
+    chunk: int = 64
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.DK)
+
+
+GDN_WORKLOADS = {
+    # long sequence, few state slices (value heads share query/key heads in pairs)
+    "gdn_long_gva_32k": GdnWorkload("gdn_long_gva_32k", 1, 32768, 8, 16, 128, 128, torch.bfloat16, 7),
+    # wide: many state slices, with an initial state
+    "gdn_wide_state_4k": GdnWorkload("gdn_wide_state_4k", 8, 4096, 16, 32, 128, 128, torch.bfloat16, 8,
+                                     init_state=True),
+}
+
+
+def make_gdn_inputs(w: GdnWorkload, device: str | torch.device = "cpu", *, B=None, T=None):
+    """Returns (q, k, v, g, beta, s0). Recipe, CPU generator seeded with w.seed, draw order:
+    q, k, v ~ N(0, 1) in fp32; q and k rows scaled to unit L2 norm (the usual normalised
+    delta-rule keys), then rounded to the dtype; per (token, value head) a gate a ~ U(0.9, 1)
+    whose log is summed inside each chunk (g, fp32); beta ~ U(0, 1) (fp32); the initial state
+    ~ N(0, 0.1^2) (fp32) when the workload has one, else None.  B and T may be overridden for
+    smaller parity cases with the same recipe."""
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    gen = torch.Generator(device="cpu").manual_seed(w.seed)
+    q = torch.randn((B, T, w.Hqk, w.DK), generator=gen)
+    k = torch.randn((B, T, w.Hqk, w.DK), generator=gen)
+    v = torch.randn((B, T, w.Hv, w.DV), generator=gen)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(w.dtype)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(w.dtype)
+    v = v.to(w.dtype)
+    a = 0.9 + 0.1 * torch.rand((B, T, w.Hv), generator=gen)
+    la = torch.log(a)
+    pad = (-T) % w.chunk
+    la = torch.nn.functional.pad(la, (0, 0, 0, pad)).reshape(B, (T + pad) // w.chunk, w.chunk, w.Hv)
+    g = la.cumsum(dim=2).reshape(B, T + pad, w.Hv)[:, :T].contiguous().float()
+    beta = torch.rand((B, T, w.Hv), generator=gen).float()
+    s0 = (0.1 * torch.randn((B, w.Hv, w.DK, w.DV), generator=gen)).float() if w.init_state else None
+    if str(device) != "cpu":
+        q, k, v, g, beta = (t.to(device) for t in (q, k, v, g, beta))
+        s0 = s0.to(device) if s0 is not None else None
+    return q, k, v, g, beta, s0

@@ -20,7 +20,10 @@ header states what is computed and which page passages each mode follows:
   (section "在线softmax"), in fp64;
 * ``attn_probs``          -- the softmax weight matrix of one (b, h);
 * ``attn_bwd``            -- gradients of O with respect to q, k, v for an upstream dO,
-  the chain rule of the definition written out (not on the pages; see the C file).
+  the chain rule of the definition written out (not on the pages; see the C file);
+* ``gdn_chunked``, ``gdn_recurrent``, ``gdn_kkt`` -- the Gated DeltaNet chunked prefill of the
+  page "lab3：GDN Prefill 前向优化" (section "算法与数据依赖"), the token recurrence it rewrites,
+  and its A = (I + L)^-1 (``gdn_oracle.c``).
 
 Every function is pinned by the ``-m "not gpu"`` tests against closed forms, page
 worked numbers, invariants and an independent library routine.
@@ -56,6 +59,12 @@ def _load():
         lib.oracle_attn_probs.argtypes = [u16p, u16p] + shape + [ci, ci, dp]
         lib.oracle_attn_bwd.argtypes = [u16p, u16p, u16p, u16p] + shape + [dp, dp, dp]
         lib.oracle_attn_bwd.restype = ci
+        gshape = [ci, ci, ci, ci, ci, ci, ci, cd]  # B, T, Hqk, Hv, DK, DV, C, scale
+        lib.oracle_gdn_recurrent.argtypes = [u16p, u16p, u16p, ci, dp, dp, dp] + gshape + [dp, dp]
+        lib.oracle_gdn_chunked.argtypes = [u16p, u16p, u16p, ci, dp, dp, dp, dp] + gshape + [dp, dp]
+        lib.oracle_gdn_kkt.argtypes = [u16p, ci, dp, dp, ci, ci, ci, ci, ci, ci, dp]
+        for f in (lib.oracle_gdn_recurrent, lib.oracle_gdn_chunked, lib.oracle_gdn_kkt):
+            f.restype = ci
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_f16.restype = cd
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
@@ -186,6 +195,74 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool, dtype: int | None = None):
     if rc != 0:
         raise ValueError("oracle_attn_bwd rejected its arguments")
     return dq, dk, dv
+
+
+def _f64(x):
+    if x is None:
+        return None
+    import torch
+
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _dp(a):
+    return None if a is None else _ptr(a, ctypes.c_double)
+
+
+def _gdn_shape(q, v):
+    B, T, Hqk, DK = q.shape
+    _, _, Hv, DV = v.shape
+    return B, T, Hqk, Hv, DK, DV
+
+
+def gdn_recurrent(q, k, v, g, beta, scale: float, s0=None, chunk: int = 64, dtype: int | None = None):
+    """Token-by-token gated delta rule. q, k [B,T,Hqk,DK]; v [B,T,Hv,DV] (fp16/bf16); g (cumulative
+    log-gate inside each chunk of `chunk` tokens) and beta [B,T,Hv]; s0 [B,Hv,DK,DV] or None.
+    Returns (o [B,T,Hv,DV], final state [B,Hv,DK,DV]) fp64."""
+    if dtype is None:
+        dtype = _dtype_code(q)
+    B, T, Hqk, Hv, DK, DV = _gdn_shape(q, v)
+    gb, bb, sb = _f64(g), _f64(beta), _f64(s0)
+    o = np.empty((B, T, Hv, DV), np.float64)
+    sf = np.empty((B, Hv, DK, DV), np.float64)
+    rc = _load().oracle_gdn_recurrent(_ptr(_bits(q), ctypes.c_uint16), _ptr(_bits(k), ctypes.c_uint16),
+                                      _ptr(_bits(v), ctypes.c_uint16), dtype, _dp(gb), _dp(bb), _dp(sb), B, T, Hqk,
+                                      Hv, DK, DV, int(chunk), float(scale), _dp(o), _dp(sf))
+    if rc != 0:
+        raise ValueError("oracle_gdn_recurrent rejected its arguments")
+    return o, sf
+
+
+def gdn_chunked(q, k, v, g, beta, A, scale: float, s0=None, chunk: int = 64, dtype: int | None = None):
+    """The page's chunk recurrence with A [B,T,Hv,chunk] given (fp64 or a tensor). Same returns."""
+    if dtype is None:
+        dtype = _dtype_code(q)
+    B, T, Hqk, Hv, DK, DV = _gdn_shape(q, v)
+    gb, bb, ab, sb = _f64(g), _f64(beta), _f64(A), _f64(s0)
+    o = np.empty((B, T, Hv, DV), np.float64)
+    sf = np.empty((B, Hv, DK, DV), np.float64)
+    rc = _load().oracle_gdn_chunked(_ptr(_bits(q), ctypes.c_uint16), _ptr(_bits(k), ctypes.c_uint16),
+                                    _ptr(_bits(v), ctypes.c_uint16), dtype, _dp(gb), _dp(bb), _dp(ab), _dp(sb), B, T,
+                                    Hqk, Hv, DK, DV, int(chunk), float(scale), _dp(o), _dp(sf))
+    if rc != 0:
+        raise ValueError("oracle_gdn_chunked rejected its arguments")
+    return o, sf
+
+
+def gdn_kkt(k, g, beta, Hv: int, chunk: int = 64, dtype: int | None = None):
+    """A [B,T,Hv,chunk] fp64: per chunk (I + L)^-1, L_ts = beta_t (k_t . k_s) exp(g_t - g_s), s < t."""
+    if dtype is None:
+        dtype = _dtype_code(k)
+    B, T, Hqk, DK = k.shape
+    gb, bb = _f64(g), _f64(beta)
+    A = np.empty((B, T, Hv, chunk), np.float64)
+    rc = _load().oracle_gdn_kkt(_ptr(_bits(k), ctypes.c_uint16), dtype, _dp(gb), _dp(bb), B, T, Hqk, Hv, DK,
+                                int(chunk), _dp(A))
+    if rc != 0:
+        raise ValueError("oracle_gdn_kkt rejected its arguments")
+    return A
 
 
 def decode(bits: int, dtype: int) -> float:

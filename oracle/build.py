@@ -1,4 +1,4 @@
-"""Compile the fp64 CPU oracle (attn_oracle.c) into oracle/liboracle.so with gcc.
+"""Compile the fp64 CPU oracles (attn_oracle.c, gdn_oracle.c) into oracle/liboracle.so with gcc.
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline use the library this builds.
@@ -8,14 +8,14 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "attn_oracle.c")
+SRCS = [os.path.join(HERE, f) for f in ("attn_oracle.c", "gdn_oracle.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
     """Always recompile; returns the path of the shared library."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-fno-fast-math", SRC, "-o", LIB + ".tmp", "-lm"]
+           "-fno-fast-math"] + SRCS + ["-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
