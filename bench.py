@@ -144,6 +144,74 @@ def time_gpu_bwd(fa, w, q, k, v, steps, warmup):
     return wall, durs, grads[0], lse
 
 
+def run_gdn(args, fa, w):
+    """Gated DeltaNet chunked prefill: A comes from gdn_kkt before the timed region (the page's
+    framework computes it outside its timing too); the timed call is gdn_chunk_fwd."""
+    import torch
+
+    from gqa_attention_forward_amd import accounting
+    from gqa_attention_forward_amd.inputs import make_gdn_inputs
+
+    q, k, v, g, beta, s0 = make_gdn_inputs(w, device="cuda")
+    _, _, A = fa.gdn_prefill(q, k, v, g, beta, s0=s0, scale=w.scale)
+    B, T, Hqk, DK = q.shape
+    Hv, DV = v.shape[2], v.shape[3]
+    o = torch.empty((B, T, Hv, DV), dtype=q.dtype, device="cuda")
+    sf = torch.empty((B, Hv, DK, DV), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    dt = 0 if q.dtype == torch.float16 else 1
+
+    def call():
+        rc = fa.gdn_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), A.data_ptr(),
+                              s0.data_ptr() if s0 is not None else None, o.data_ptr(), sf.data_ptr(), B, T, Hqk, Hv,
+                              DK, DV, w.scale, dt, stream.cuda_stream)
+        assert rc == 0, rc
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    avg_ms = sum(durs) / len(durs)
+    flops = accounting.gdn_flops(B, T, Hv, DK, DV)
+    nbytes = accounting.gdn_bytes(B, T, Hqk, Hv, DK, DV, s0 is not None)
+    assert torch.isfinite(sf).all().item(), "non-finite state"
+    line = {"workload": w.name, "path": "gdn_chunk_fwd", "ms": round(avg_ms, 4),
+            "median_ms": round(durs[len(durs) // 2], 4), "tflops": round(flops / (avg_ms * 1e-3) / 1e12, 2),
+            "compulsory_gbs": round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
+            "workgroups": B * Hv * (DV // 64)}
+    print(json.dumps(line), file=sys.stderr, flush=True)
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    return {
+        "metric": "Gated DeltaNet chunked prefill ms per call and TFLOPS (algorithmic chunk products)",
+        "value": round(flops * args.steps / wall / 1e12, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "T": T, "Hqk": Hqk, "Hv": Hv, "DK": DK, "DV": DV,
+                   "init_state": s0 is not None, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_avg_us": round(avg_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+
+
 def cpu_baseline(w, q, k, v, target_s):
     """Times the oracle (as it stands) on a random sample of rows of the workload."""
     import numpy as np
@@ -227,9 +295,16 @@ def main():
     split_kv = {"auto": "auto", "off": False}.get(args.split_kv)
     if split_kv is None:
         split_kv = int(args.split_kv)
-    names = list(WORKLOADS) if args.all else [args.workload]
+    from gqa_attention_forward_amd.inputs import GDN_WORKLOADS
+
+    names = (list(WORKLOADS) + (list(GDN_WORKLOADS) if args.which == "fwd" else [])) if args.all else [args.workload]
     result = None
     for name in names:
+        if name in GDN_WORKLOADS:
+            r = run_gdn(args, fa, GDN_WORKLOADS[name])
+            if name == args.workload:
+                result = r
+            continue
         w = WORKLOADS[name]
         q, k, v, _ = make_inputs(w, device="cuda")
         if args.layout == "bshd":  # the same values in [B, S, H, D] buffers, passed as [B, H, S, D] views

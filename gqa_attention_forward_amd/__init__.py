@@ -77,6 +77,11 @@ def _load():
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp, sz, vp]
     lib.fa_bwd.restype = ci
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.gdn_kkt.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
+    lib.gdn_kkt.restype = ci
+    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.gdn_chunk_fwd.restype = ci
     _lib = lib
     return lib
 
@@ -143,6 +148,17 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, M, N, D, scale, causal
     """Raw C ABI call of the backward pass (pointers as integers)."""
     return _load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, M, N, D, float(scale), int(causal),
                           int(dtype), workspace, int(workspace_bytes), stream)
+
+
+def gdn_kkt(k, g, beta, A, B, T, Hqk, Hv, DK, dtype, stream) -> int:
+    """Raw C ABI call (include/gdn.h): A = (I + L)^-1 per 64-token chunk."""
+    return _load().gdn_kkt(k, g, beta, A, B, T, Hqk, Hv, DK, int(dtype), stream)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, stream) -> int:
+    """Raw C ABI call (include/gdn.h): the Gated DeltaNet chunk recurrence."""
+    return _load().gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, float(scale), int(dtype),
+                                 stream)
 
 
 def fa_strerror(code: int) -> str:
@@ -285,5 +301,41 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     return dq, dk, dv
 
 
-__all__ = ["fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, stream=None):
+    """Gated DeltaNet chunked prefill on contiguous device tensors: q, k [B,T,Hqk,128], v [B,T,Hv,DV]
+    (fp16/bf16), g and beta [B,T,Hv] fp32 (g: cumulative log-gate inside each 64-token chunk),
+    s0 [B,Hv,128,DV] fp32 or None.  A [B,T,Hv,64] (dtype) is computed with gdn_kkt when not given.
+    Returns (o [B,T,Hv,DV], final state [B,Hv,128,DV] fp32, A)."""
+    import torch
+
+    B, T, Hqk, DK = q.shape
+    _, _, Hv, DV = v.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("g and beta must be float32")
+    if s0 is not None and (s0.dtype != torch.float32 or not s0.is_contiguous()):
+        raise TypeError("s0 must be a contiguous float32 tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(DK)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    dt = _dtype_code(q)
+    if A is None:
+        A = torch.empty((B, T, Hv, 64), dtype=q.dtype, device=q.device)
+        rc = gdn_kkt(k.data_ptr(), g.data_ptr(), beta.data_ptr(), A.data_ptr(), B, T, Hqk, Hv, DK, dt, stream)
+        if rc != FA_OK:
+            raise FaError(rc, "gdn_kkt")
+    o = torch.empty((B, T, Hv, DV), dtype=q.dtype, device=q.device)
+    sf = torch.empty((B, Hv, DK, DV), dtype=torch.float32, device=q.device)
+    rc = gdn_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), A.data_ptr(),
+                       s0.data_ptr() if s0 is not None else None, o.data_ptr(), sf.data_ptr(), B, T, Hqk, Hv, DK, DV,
+                       scale, dt, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "gdn_chunk_fwd")
+    return o, sf, A
+
+
+__all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_prefill", "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]

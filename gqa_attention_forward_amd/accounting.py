@@ -32,3 +32,28 @@ def workload_flops(w) -> int:
 
 def workload_bytes(w) -> int:
     return compulsory_bytes(w.B, w.Hq, w.Hkv, w.M, w.N, w.D)
+
+
+# ------------------------------------------------------------ Gated DeltaNet chunked prefill
+
+def gdn_flops(B: int, T: int, Hv: int, DK: int, DV: int, chunk: int = 64) -> float:
+    """Algorithmic flops of the chunk recurrence, per value head and chunk of n tokens (2 flops
+    per multiply-add): U' = K S (n DK DV), Q S (n DK DV), the scores Q K^T (n n DK),
+    V_new = A W' (n n DV), scores V_new (n n DV), the state update K^T V_new (DK n DV)."""
+    total = 0.0
+    for c0 in range(0, T, chunk):
+        n = min(chunk, T - c0)
+        total += 2.0 * (3 * n * DK * DV + n * n * DK + 2 * n * n * DV)
+    return total * B * Hv
+
+
+def gdn_bytes(B: int, T: int, Hqk: int, Hv: int, DK: int, DV: int, init_state: bool, chunk: int = 64,
+              elem: int = 2) -> int:
+    """Compulsory HBM bytes of one chunk-recurrence call: q, k, v, A read once, g and beta (fp32)
+    read once, the initial state read (if any) and the final state written (fp32), o written."""
+    qk = 2 * B * T * Hqk * DK * elem
+    vo = 2 * B * T * Hv * DV * elem
+    a = B * T * Hv * chunk * elem
+    gb = 2 * B * T * Hv * 4
+    st = B * Hv * DK * DV * 4 * (2 if init_state else 1)
+    return qk + vo + a + gb + st

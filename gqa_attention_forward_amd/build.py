@@ -9,7 +9,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "gdn_fwd.hip")]
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
 

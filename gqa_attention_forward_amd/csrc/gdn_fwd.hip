@@ -1,0 +1,478 @@
+// gdn_fwd.hip -- Gated DeltaNet chunked prefill for MI355X (gfx950): the chunk recurrence of the
+// page "lab3：GDN Prefill 前向优化", section "算法与数据依赖", and the per-chunk triangular solve
+// that produces its A input.
+//
+// Per value head h (reading query/key head h / (Hv / Hqk)) and 64-token chunk c, with g the
+// gate's cumulative log inside the chunk:
+//     U' = K S_c;  W' = beta (V - exp(g) U');  V_new = A W';
+//     O  = scale (exp(g) (Q S_c) + scores V_new),  scores_ts = (q_t . k_s) exp(g_t - g_s), s <= t;
+//     S_{c+1} = exp(g_last) S_c + (K exp(g_last - g))^T V_new,
+// with A = (I + L)^-1, L_ts = beta_t (k_t . k_s) exp(g_t - g_s) for s < t.
+//
+// chunk_kernel: one workgroup (4 waves) per (b, value head, 64 columns of the state), walking the
+// chunks in order -- the state is the only thing carried from chunk to chunk, and each slice of
+// it is independent, as the page's split of the state over (batch, V head, DV block) notes.
+// The fp32 state lives in MFMA accumulators for the whole sequence; each chunk a bf16 copy
+// goes to LDS as the operand of U' and Q S (operands bf16/fp16, accumulation and state fp32,
+// as on the page).  The six products per chunk run on the 32x32x16 MFMA with every operand
+// read from LDS; a result that feeds a later product as its B operand is written to LDS
+// transposed (a lane's accumulator column holds 4 consecutive rows per register group, so the
+// transposed write is 8 bytes).  Q and K tiles use the XOR-swizzled layout because K is also
+// read transposed (K^T of the state update); the next chunk's Q, K, A, g and beta are copied
+// HBM -> LDS by buffer loads while the current chunk computes.
+//
+// kkt_kernel: one workgroup per (b, value head, chunk): K K^T on MFMA, L, then the unit lower
+// triangular inverse by forward substitution, one lane per column of A, in registers.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_device.h"
+#include "fa_swizzle.h"
+#include "gdn.h"
+
+namespace fa {
+namespace gdn {
+
+constexpr int C = 64;     // chunk length
+constexpr int DK = 128;   // query/key head dim
+constexpr int DVB = 64;   // state columns a workgroup owns
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float exp_(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// Row order of a 32-row A operand that makes accumulator register r of lane half hh hold row
+// 16 hh + r (the accumulator row of register r in half hh is 8 (r / 4) + 4 hh + r % 4).
+__device__ __forceinline__ constexpr int perm32(int i) { return 16 * ((i >> 2) & 1) + ((i >> 3) << 2) + (i & 3); }
+
+// one element rounded to T, as its 16 bits
+template <typename T> __device__ __forceinline__ unsigned short bits16(float x)
+{
+    return (unsigned short)(Elem<T>::pack2(x, 0.f) & 0xffffu);
+}
+
+// 4-byte-per-lane buffer load into LDS: lane i writes dst + 4 i
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t rs, lds_void *dst, unsigned voffset)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voffset, 0, 0, 0);
+#endif
+}
+
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+// s_waitcnt vmcnt(0): every load (and store) this wave issued has completed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, long long bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)(bytes > 0 ? bytes : 0), 0x00020000);
+}
+
+// ----------------------------------------------------------------- KKT solve
+
+struct KktParams {
+    const void *k;
+    const float *g, *beta;
+    void *A;
+    int B, T, Hqk, Hv, n_chunks;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void kkt_kernel(KktParams p)
+{
+    constexpr int KP = 17 * 16;  // K row pitch in bytes: odd units, conflict-free 16-byte row reads
+    constexpr int LP = 68;       // L row pitch in floats
+    __shared__ __attribute__((aligned(16))) unsigned char kt_raw[C * KP];
+    __shared__ __attribute__((aligned(16))) float L[C * LP];
+    __shared__ float X[C * (C + 1)];  // the inverse, X[t][j] at t * (C + 1) + j
+    __shared__ float gs[C], bs[C];
+    lds_u8 *kt = (lds_u8 *)kt_raw;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = (int)(blockIdx.x % p.n_chunks);
+    const long long bh = blockIdx.x / p.n_chunks;
+    const int b = (int)(bh / p.Hv), h = (int)(bh % p.Hv), hk = h / (p.Hv / p.Hqk);
+    const int t0 = c * C, n = p.T - t0 < C ? p.T - t0 : C;
+
+    for (int i = tid; i < C * (DK / 8); i += 256) {  // 64 rows x 16 units; rows past n are zero
+        const int r = i >> 4, u = i & 15;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < n) v = *(const u32x4 *)((const T *)p.k + (((size_t)b * p.T + t0 + r) * p.Hqk + hk) * DK + u * 8);
+        *(lds_u32x4 *)(kt + r * KP + u * 16) = v;
+    }
+    if (tid < C) {
+        const size_t idx = ((size_t)b * p.T + t0 + tid) * p.Hv + h;
+        gs[tid] = tid < n ? p.g[idx] : 0.f;
+        bs[tid] = tid < n ? p.beta[idx] : 0.f;
+    }
+    __syncthreads();
+
+    // K K^T: wave w computes the 32x32 block (rows t in 32 tb, columns s in 32 sb)
+    {
+        const int tb = wave >> 1, sb = wave & 1, ql = lane & 31, hh = lane >> 5;
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks) {
+            const u32x4 a = *(const lds_u32x4 *)(kt + (32 * tb + ql) * KP + (2 * ks + hh) * 16);
+            const u32x4 bb = *(const lds_u32x4 *)(kt + (32 * sb + ql) * KP + (2 * ks + hh) * 16);
+            acc = Elem<T>::mfma(a, bb, acc);
+        }
+        const int s = 32 * sb + ql;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = 32 * tb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            L[t * LP + s] = (s < t && t < n) ? bs[t] * acc[r] * exp_(gs[t] - gs[s]) : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // (I + L) X = I, one lane per column j: X_tj = [t == j] - sum_{s < t} L_ts X_sj.  A lane reads
+    // only its own column of X (and L rows broadcast), so one wave needs no barrier.  L's row t
+    // is zero from column t on, so the sum runs over whole groups of 4.
+    if (wave == 0) {
+        const int j = lane;
+        for (int t = 0; t < C; ++t) {
+            float x = t == j ? 1.f : 0.f;
+            for (int s4 = 0; s4 < t; s4 += 4) {
+                const f32x4 l4 = *(const f32x4 *)(L + t * LP + s4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x = __builtin_fmaf(-l4[e], X[(s4 + e) * (C + 1) + j], x);
+            }
+            X[t * (C + 1) + j] = x;
+        }
+        unsigned short *out = (unsigned short *)p.A;
+        for (int t = 0; t < n; ++t) out[(((size_t)b * p.T + t0 + t) * p.Hv + h) * C + j] = bits16<T>(X[t * (C + 1) + j]);
+    }
+}
+
+// ---------------------------------------------------------------- chunk kernel
+
+struct ChunkParams {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const void *A;
+    const float *s0;  // may be null
+    void *o;
+    float *s_final;
+    int B, T, Hqk, Hv, DV, n_chunks, dv_blocks;
+    float scale;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
+{
+    // LDS: two input buffers [Q | K | A | g | beta] and the per-chunk work arrays
+    constexpr int QK_TILE = C * DK * 2;        // swizzled, 256-byte rows
+    constexpr int AP = 9 * 16;                 // A / work-array pitch in bytes (64 elements + pad)
+    constexpr int A_TILE = C * AP;
+    constexpr int BUF = 2 * QK_TILE + A_TILE + 2 * 256;
+    constexpr int SP = 17 * 16;                // St pitch: 128 elements + pad
+    constexpr int OFF_ST = 2 * BUF, OFF_WT = OFF_ST + DVB * SP, OFF_SC = OFF_WT + DVB * AP,
+                  OFF_VN = OFF_SC + C * AP, OFF_VH = OFF_VN + DVB * AP, SMEM = OFF_VH + DVB * AP;
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM];
+    lds_u8 *smem = (lds_u8 *)smem_raw;
+    lds_u8 *st = smem + OFF_ST, *wt = smem + OFF_WT, *sc = smem + OFF_SC, *vn = smem + OFF_VN,
+           *vh = smem + OFF_VH;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ql = lane & 31, hh = lane >> 5;
+    const int tb = wave >> 1, cb = wave & 1;  // this wave's 32x32 output block of the chunk products
+    const int dvblk = (int)(blockIdx.x % p.dv_blocks);
+    const long long bh = blockIdx.x / p.dv_blocks;
+    const int b = (int)(bh / p.Hv), h = (int)(bh % p.Hv), hk = h / (p.Hv / p.Hqk);
+    const int dv0 = dvblk * DVB;
+    const int T_ = p.T, Hv = p.Hv, DV = p.DV;
+    const long long qk_rs = (long long)p.Hqk * DK * sizeof(T);  // row stride of q / k in bytes
+    const long long a_rs = (long long)Hv * C * sizeof(T);
+    const T *qbase = (const T *)p.q + ((size_t)b * T_ * p.Hqk + hk) * DK;
+    const T *kbase = (const T *)p.k + ((size_t)b * T_ * p.Hqk + hk) * DK;
+    const T *abase = (const T *)p.A + ((size_t)b * T_ * Hv + h) * C;
+    const float *gbase = p.g + (size_t)b * T_ * Hv + h, *bbase = p.beta + (size_t)b * T_ * Hv + h;
+
+    // per-lane source offsets of the tile copies (see the 1 KiB-per-instruction layout notes in
+    // the backward kernels): Q/K instruction j = wave + 4 i fills rows 4 j .. 4 j + 3
+    const int qk_row = 4 * wave + (lane >> 4), qk_phys = lane & 15;
+    const unsigned qk_src = (unsigned)(qk_row * qk_rs + ((qk_phys ^ swz<DK>(qk_row)) * 16));
+    unsigned a_src[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {  // A instruction j = wave + 4 i (< 9) fills units 64 j .. 64 j + 63
+        const int u = (wave + 4 * i) * 64 + lane, row = u / 9, unit = u % 9;
+        a_src[i] = unit < 8 && row < C ? (unsigned)(row * a_rs + unit * 16) : 0x7fffff00u;
+    }
+    auto issue = [&](int c, int buf) {
+        const int t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
+        lds_u8 *dst = smem + buf * BUF;
+        const __amdgpu_buffer_rsrc_t rq = rsrc(qbase + (size_t)t0 * p.Hqk * DK, (n - 1) * qk_rs + DK * sizeof(T));
+        const __amdgpu_buffer_rsrc_t rk = rsrc(kbase + (size_t)t0 * p.Hqk * DK, (n - 1) * qk_rs + DK * sizeof(T));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned off = qk_src + (unsigned)(16 * i * qk_rs);
+            lds_load16(rq, (lds_void *)(dst + (wave + 4 * i) * 1024), off);
+            lds_load16(rk, (lds_void *)(dst + QK_TILE + (wave + 4 * i) * 1024), off);
+        }
+        const __amdgpu_buffer_rsrc_t ra = rsrc(abase + (size_t)t0 * Hv * C, (n - 1) * a_rs + C * sizeof(T));
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            if (wave + 4 * i < 9) lds_load16(ra, (lds_void *)(dst + 2 * QK_TILE + (wave + 4 * i) * 1024), a_src[i]);
+        if (wave < 2) {  // g (wave 0) and beta (wave 1): 64 floats, one per lane
+            const float *src = (wave == 0 ? gbase : bbase) + (size_t)t0 * Hv;
+            lds_load4(rsrc(src, (long long)(n - 1) * Hv * 4 + 4), (lds_void *)(dst + 2 * QK_TILE + A_TILE + wave * 256),
+                      (unsigned)(lane * Hv * 4));
+        }
+    };
+    // V of this wave's block: column dv0 + 32 cb + ql, rows 32 tb + 8 q + 4 hh + e
+    auto load_v = [&](int c, unsigned short (&vr)[16]) {
+        const int t0 = c * C;
+        const unsigned short *vb = (const unsigned short *)p.v;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = t0 + 32 * tb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            vr[r] = t < T_ ? vb[(((size_t)b * T_ + t) * Hv + h) * DV + dv0 + 32 * cb + ql] : (unsigned short)0;
+        }
+    };
+
+    // state: wave w owns state rows (key dims) 32 w .. 32 w + 31 for both 32-column blocks j;
+    // accumulator register r of half hh is row 32 w + 16 hh + r (the transposing read's order)
+    f32x16 S[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = 32 * wave + 16 * hh + r, e = dv0 + 32 * j + ql;
+            S[j][r] = p.s0 ? p.s0[((size_t)bh * DK + d) * DV + e] : 0.f;
+        }
+    // bf16 copy of the state, transposed: St[column][key dim], 16 consecutive key dims per lane
+    auto write_st = [&]() {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            u32x4 w0, w1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                w0[r] = Elem<T>::pack2(S[j][2 * r], S[j][2 * r + 1]);
+                w1[r] = Elem<T>::pack2(S[j][8 + 2 * r], S[j][8 + 2 * r + 1]);
+            }
+            lds_u8 *dst = st + (32 * j + ql) * SP + (32 * wave + 16 * hh) * 2;
+            *(lds_u32x4 *)dst = w0;
+            *(lds_u32x4 *)(dst + 16) = w1;
+        }
+    };
+    // 8-byte transposed write: 4 accumulator rows (registers 4 q .. 4 q + 3) of column `col`
+    auto put4 = [&](lds_u8 *arr, int pitch, int col, int row0, float x0, float x1, float x2, float x3) {
+        u32x2 w;
+        w[0] = Elem<T>::pack2(x0, x1);
+        w[1] = Elem<T>::pack2(x2, x3);
+        *(__attribute__((address_space(3))) u32x2 *)(arr + col * pitch + row0 * 2) = w;
+    };
+    auto row16 = [&](const lds_u8 *arr, int pitch, int row, int unit) {
+        return *(const lds_u32x4 *)(arr + row * pitch + unit * 16);
+    };
+
+    const TrOffsets<DK> tro(lane);
+    const float scale = p.scale;
+    unsigned short vcur[16], vnext[16];
+    issue(0, 0);
+    load_v(0, vcur);
+    write_st();
+    wait_vm0();
+    __syncthreads();
+
+    for (int c = 0; c < p.n_chunks; ++c) {
+        const int buf = c & 1, t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
+        if (c + 1 < p.n_chunks) {
+            issue(c + 1, buf ^ 1);
+            load_v(c + 1, vnext);
+        }
+        const lds_u8 *qt = smem + buf * BUF, *kt = qt + QK_TILE, *at = kt + QK_TILE;
+        const lds_f32 *gl = (const lds_f32 *)(at + A_TILE), *bl = gl + C;
+
+        // ---- U' = K S_c, Q S_c and K Q^T (this wave's blocks)
+        // The output is computed transposed, O^T = S^T Q^T (+ V_new^T scores^T below), with the
+        // state's rows read in perm32 order: lane (t = 32 tb + ql, hh) then holds the 16
+        // consecutive columns 32 cb + 16 hh .. + 15 of its token and stores them as 32 bytes.
+        f32x16 U, O, KQ;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) U[r] = O[r] = KQ[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks) {
+            const int u = 2 * ks + hh;
+            const u32x4 sb = row16(st, SP, 32 * cb + ql, u);
+            const u32x4 ka = read_row<DK>(kt, 32 * tb + ql, u);
+            const u32x4 qa = read_row<DK>(qt, 32 * tb + ql, u);
+            U = Elem<T>::mfma(ka, sb, U);
+            O = Elem<T>::mfma(row16(st, SP, 32 * cb + perm32(ql), u), qa, O);
+            KQ = Elem<T>::mfma(ka, read_row<DK>(qt, 32 * cb + ql, u), KQ);
+        }
+        {
+            const float eg = exp_(gl[32 * tb + ql]);  // O^T column t = 32 tb + ql
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[r] *= eg;
+        }
+        // rows t (or s) = 32 tb + 8 q + 4 hh + e; columns dv (or t) = 32 cb + ql
+        const float g_col = gl[32 * cb + ql];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r0 = 32 * tb + 8 * q + 4 * hh;
+            const f32x4 g4 = *(const lds_f32x4 *)(gl + r0), b4 = *(const lds_f32x4 *)(bl + r0);
+            float w[4], s4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q + e;
+                const float eg = exp_(g4[e]);
+                const f32x2 vv = Elem<T>::unpack2((unsigned)vcur[r]);
+                w[e] = b4[e] * (vv[0] - eg * U[r]);
+                // scores[t][s] for t = column, s = row: causal and gate-decayed
+                s4[e] = r0 + e <= 32 * cb + ql ? KQ[r] * exp_(g_col - g4[e]) : 0.f;
+            }
+            put4(wt, AP, 32 * cb + ql, r0, w[0], w[1], w[2], w[3]);
+            put4(sc, AP, 32 * cb + ql, r0, s4[0], s4[1], s4[2], s4[3]);
+        }
+        __syncthreads();
+
+        // ---- V_new = A W'
+        f32x16 V;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) V[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks)
+            V = Elem<T>::mfma(row16(at, AP, 32 * tb + ql, 2 * ks + hh), row16(wt, AP, 32 * cb + ql, 2 * ks + hh), V);
+        const float g_last = gl[n - 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r0 = 32 * tb + 8 * q + 4 * hh;
+            const f32x4 g4 = *(const lds_f32x4 *)(gl + r0);
+            put4(vn, AP, 32 * cb + ql, r0, V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);
+            // decayed copy for the state update, positions with bits 2 and 3 of s swapped so that
+            // the 8 rows one transposing K read pairs with are 16 contiguous bytes
+            const int p0 = 32 * tb + 16 * (q >> 1) + 8 * hh + 4 * (q & 1);
+            put4(vh, AP, 32 * cb + ql, p0, V[4 * q] * exp_(g_last - g4[0]), V[4 * q + 1] * exp_(g_last - g4[1]),
+                 V[4 * q + 2] * exp_(g_last - g4[2]), V[4 * q + 3] * exp_(g_last - g4[3]));
+        }
+        __syncthreads();
+
+        // ---- O = scale (exp(g) Q S_c + scores V_new)
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks)
+            O = Elem<T>::mfma(row16(vn, AP, 32 * cb + perm32(ql), 2 * ks + hh), row16(sc, AP, 32 * tb + ql, 2 * ks + hh),
+                              O);
+        if (32 * tb + ql < n) {
+            u32x4 w0, w1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                w0[r] = Elem<T>::pack2(O[2 * r] * scale, O[2 * r + 1] * scale);
+                w1[r] = Elem<T>::pack2(O[8 + 2 * r] * scale, O[8 + 2 * r + 1] * scale);
+            }
+            u32x4 *dst = (u32x4 *)((T *)p.o + (((size_t)b * T_ + t0 + 32 * tb + ql) * Hv + h) * DV + dv0 + 32 * cb +
+                                   16 * hh);
+            dst[0] = w0;
+            dst[1] = w1;
+        }
+        // ---- S_{c+1} = exp(g_last) S_c + K^T (exp(g_last - g) V_new)
+        const float decay = exp_(g_last);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[j][r] *= decay;
+#pragma unroll
+            for (int sblk = 0; sblk < 2; ++sblk)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const u32x4 a = read_tr<DK>(kt, tro, 32 * sblk + 16 * tt, wave);
+                    const u32x4 bv = *(const lds_u32x4 *)(vh + (32 * j + ql) * AP + (32 * sblk + 16 * tt + 8 * hh) * 2);
+                    S[j] = Elem<T>::mfma(a, bv, S[j]);
+                }
+        }
+        __syncthreads();  // every wave is done reading St, W', scores, V_new of this chunk
+        write_st();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) vcur[r] = vnext[r];
+        wait_vm0();       // the next chunk's tiles (and this chunk's output stores) have landed
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = 32 * wave + 16 * hh + r, e = dv0 + 32 * j + ql;
+            p.s_final[((size_t)bh * DK + d) * DV + e] = S[j][r];
+        }
+}
+
+}  // namespace gdn
+}  // namespace fa
+
+extern "C" {
+
+int gdn_kkt(const void *k, const float *g, const float *beta, void *A, int B, int T, int Hqk, int Hv, int DK,
+            int dtype, void *stream)
+{
+    if (!k || !g || !beta || !A || B <= 0 || T <= 0 || Hqk <= 0 || Hv <= 0 || DK <= 0) return FA_ERR_INVALID_ARG;
+    if (Hv % Hqk != 0 || (dtype != FA_F16 && dtype != FA_BF16)) return FA_ERR_INVALID_ARG;
+    if (DK != fa::gdn::DK) return FA_ERR_UNSUPPORTED;
+    if (((uintptr_t)k | (uintptr_t)A) & 15u) return FA_ERR_UNSUPPORTED;
+    fa::gdn::KktParams p;
+    p.k = k;
+    p.g = g;
+    p.beta = beta;
+    p.A = A;
+    p.B = B;
+    p.T = T;
+    p.Hqk = Hqk;
+    p.Hv = Hv;
+    p.n_chunks = (T + fa::gdn::C - 1) / fa::gdn::C;
+    const long long grid = (long long)B * Hv * p.n_chunks;
+    if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == FA_F16)
+        hipLaunchKernelGGL((fa::gdn::kkt_kernel<_Float16>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((fa::gdn::kkt_kernel<__bf16>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *A,
+                  const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv, int DK, int DV, float scale,
+                  int dtype, void *stream)
+{
+    if (!q || !k || !v || !g || !beta || !A || !o || !s_final) return FA_ERR_INVALID_ARG;
+    if (B <= 0 || T <= 0 || Hqk <= 0 || Hv <= 0 || DK <= 0 || DV <= 0 || Hv % Hqk != 0) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale) || (dtype != FA_F16 && dtype != FA_BF16)) return FA_ERR_INVALID_ARG;
+    if (DK != fa::gdn::DK || DV % fa::gdn::DVB != 0) return FA_ERR_UNSUPPORTED;
+    const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)A | (uintptr_t)o |
+                         (uintptr_t)s_final | (uintptr_t)s0 | (uintptr_t)g | (uintptr_t)beta;
+    if (al & 15u) return FA_ERR_UNSUPPORTED;
+    // tile copies use 32-bit offsets inside one chunk: 63 rows of q/k, A, g and beta
+    if ((long long)Hqk * fa::gdn::DK * 2 * 64 > 0x7fff0000LL || (long long)Hv * 64 * 2 * 64 > 0x7fff0000LL)
+        return FA_ERR_UNSUPPORTED;
+    fa::gdn::ChunkParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.A = A;
+    p.s0 = s0;
+    p.o = o;
+    p.s_final = s_final;
+    p.B = B;
+    p.T = T;
+    p.Hqk = Hqk;
+    p.Hv = Hv;
+    p.DV = DV;
+    p.n_chunks = (T + fa::gdn::C - 1) / fa::gdn::C;
+    p.dv_blocks = DV / fa::gdn::DVB;
+    p.scale = scale;
+    const long long grid = (long long)B * Hv * p.dv_blocks;
+    if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == FA_F16)
+        hipLaunchKernelGGL((fa::gdn::chunk_kernel<_Float16>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((fa::gdn::chunk_kernel<__bf16>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

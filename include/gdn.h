@@ -1,0 +1,57 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet chunked prefill in libfa.so (MI355X, gfx950).
+ *
+ * Source: the page "lab3：GDN Prefill 前向优化", section "算法与数据依赖": chunks of 64 tokens,
+ * head dim 128, the framework-side inputs g (the gate's cumulative log inside each chunk) and
+ * A (the "KKT" triangular-solve result), and the chunk recurrence, per value head h reading
+ * query/key head h / (Hv / Hqk) (the page's GVA mapping):
+ *     U' = K S_c;  W' = beta (V - exp(g) U');  V_new = A W';
+ *     O  = scale (exp(g) (Q S_c) + scores V_new),  scores_ts = (q_t . k_s) exp(g_t - g_s) for s <= t;
+ *     S_{c+1} = exp(g_last) S_c + (K exp(g_last - g))^T V_new.
+ * Reading taken (the page names A but does not print it): A = (I + L)^-1 per chunk with
+ * L_ts = beta_t (k_t . k_s) exp(g_t - g_s) for s < t and 0 otherwise -- beta and the gate decay
+ * folded in, as the page's note on its rejected FlashQLA port says its inputs have -- which makes
+ * the chunk recurrence equal to the token-by-token gated delta rule
+ *     S <- a_t S;  u_t = beta_t (v_t - S^T k_t);  S <- S + k_t u_t^T;  o_t = scale S^T q_t,
+ * with a_t = exp(g_t - g_{t-1}) inside a chunk (g_{-1} = 0 at a chunk start).
+ *
+ * Layouts (contiguous, DEVICE memory owned by the caller):
+ *   q, k   [B, T, Hqk, DK]  fp16 or bf16 (dtype as in fa.h)     DK must be 128
+ *   v      [B, T, Hv, DV]   same dtype                            DV a multiple of 64
+ *   g      [B, T, Hv]  fp32: cumulative log-gate inside each chunk [64 c, 64 c + 64) (T need not
+ *          be a multiple of 64: the last chunk is shorter)
+ *   beta   [B, T, Hv]  fp32
+ *   A      [B, T, Hv, 64]  dtype: row t holds row (t mod 64) of its chunk's 64 x 64 matrix; columns
+ *          past the chunk's end are ignored
+ *   s0     [B, Hv, DK, DV] fp32 initial state, or NULL for zeros
+ *   o      [B, T, Hv, DV]  dtype, written;  s_final [B, Hv, DK, DV] fp32, written
+ * All pointers 16-byte aligned.  Hv must be a multiple of Hqk.
+ *
+ * gdn_kkt: computes A from k, g, beta (K K^T in fp32 on MFMA, the inverse by forward
+ *   substitution in fp32, rounded to dtype once).  One kernel on `stream`.
+ * gdn_chunk_fwd: the chunk recurrence; one kernel on `stream`, one workgroup per (b, value head,
+ *   64 state columns) walking the chunks in order.  Operands of the products are rounded to
+ *   dtype (the state's operand copy included); accumulation and the state itself are fp32.
+ * Both validate every argument before any HIP call (FA_ERR_INVALID_ARG: null pointer, bad size,
+ * Hv % Hqk, scale not finite or <= 0, unknown dtype; FA_ERR_UNSUPPORTED: DK != 128, DV not a
+ * multiple of 64, misaligned pointer, strides beyond 32-bit tile offsets), return FA_ERR_LAUNCH if
+ * the launch fails, allocate nothing and do not synchronise.  Deterministic.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int gdn_kkt(const void *k, const float *g, const float *beta, void *A, int B, int T, int Hqk, int Hv, int DK,
+            int dtype, void *stream);
+int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *A,
+                  const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv, int DK, int DV, float scale,
+                  int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

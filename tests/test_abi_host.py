@@ -8,18 +8,21 @@ import pytest
 
 import gqa_attention_forward_amd as fa
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names.update(re.findall(r"\b((?:fa|gdn)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = _declared()
-    assert "fa_fwd" in names and "fa_strerror" in names
+    assert {"fa_fwd", "fa_strerror", "fa_bwd", "gdn_kkt", "gdn_chunk_fwd"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -171,3 +174,32 @@ def test_strided_split_invalid():
     rc = fa.fa_fwd_splitkv_strided(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 1, 2, 1, 16, 16, 64, None, st, None, None,
                                    0.125, 1, 0, 1, None, 0, None)
     assert rc == fa.FA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ Gated DeltaNet entry points
+
+GDN = dict(q=0x1000, k=0x2000, v=0x3000, g=0x4000, beta=0x5000, A=0x6000, s0=None, o=0x7000, sf=0x8000,
+           B=1, T=64, Hqk=1, Hv=2, DK=128, DV=128, scale=0.1, dtype=1)
+
+
+def _gdn(**kw):
+    a = dict(GDN)
+    a.update(kw)
+    return fa.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A"], a["s0"], a["o"], a["sf"], a["B"],
+                            a["T"], a["Hqk"], a["Hv"], a["DK"], a["DV"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("bad", [dict(q=None), dict(A=None), dict(sf=None), dict(T=0), dict(Hqk=2, Hv=3),
+                                 dict(scale=0.0), dict(dtype=5)])
+def test_gdn_invalid(bad):
+    assert _gdn(**bad) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(DK=64), dict(DV=96), dict(v=0x3008), dict(s0=0x9004)])
+def test_gdn_unsupported(bad):
+    assert _gdn(**bad) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_gdn_kkt_invalid():
+    assert fa.gdn_kkt(None, 0x4000, 0x5000, 0x6000, 1, 64, 1, 2, 128, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.gdn_kkt(0x2000, 0x4000, 0x5000, 0x6000, 1, 64, 1, 2, 64, 1, None) == fa.FA_ERR_UNSUPPORTED

@@ -1,0 +1,101 @@
+"""Parity of the Gated DeltaNet kernels (through the C ABI) against the fp64 oracle.
+
+gdn_kkt: A against the oracle's (I + L)^-1, within the rounding of A to the input type
+(max-abs error <= 2^-7 max(1, max|A|) for bf16, 2^-10 for fp16: half an ulp plus the fp32 solve).
+gdn_chunk_fwd: output and final state against the oracle's chunk recurrence fed the same A (the
+GPU's, decoded), within the page's 5e-3 max error scaled by the reference's magnitude (floor 1);
+and against the token-by-token recurrence (exact A) within twice that.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_forward_amd as fa
+import oracle
+from gqa_attention_forward_amd.inputs import GDN_WORKLOADS, GdnWorkload, make_gdn_inputs
+
+pytestmark = pytest.mark.gpu
+
+A_TOL = {torch.bfloat16: 2.0 ** -7, torch.float16: 2.0 ** -10}
+TOL = 5e-3
+
+
+def _case(B, T, Hqk, Hv, DV, dtype, init, seed):
+    w = GdnWorkload("t", B, T, Hqk, Hv, 128, DV, dtype, seed, init_state=init)
+    return w, make_gdn_inputs(w)
+
+
+def _err(got, ref, what):
+    m = max(1.0, float(np.abs(ref).max()))
+    e = float(np.abs(got - ref).max())
+    print(f"{what}: max|err| {e:.3e}, max|ref| {np.abs(ref).max():.3e}", flush=True)
+    return e / m
+
+
+CASES = [
+    # B, T, Hqk, Hv, DV, dtype, init_state
+    (1, 64, 1, 1, 64, torch.bfloat16, False),
+    (1, 200, 2, 4, 128, torch.bfloat16, True),    # ragged last chunk, value heads in pairs
+    (2, 256, 1, 3, 64, torch.float16, True),      # three value heads per key head
+    (1, 1000, 4, 4, 128, torch.bfloat16, False),  # 16 chunks
+    (1, 1, 1, 2, 64, torch.float16, False),        # one token
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(str(x) for x in c[:5]) + str(c[5])[-4:] + str(c[6]))
+def test_gdn_matches_oracle(case):
+    B, T, Hqk, Hv, DV, dtype, init = case
+    w, (q, k, v, g, beta, s0) = _case(B, T, Hqk, Hv, DV, dtype, init, seed=T + Hv)
+    dev = [t.cuda() if t is not None else None for t in (q, k, v, g, beta, s0)]
+    o, sf, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale)
+    torch.cuda.synchronize()
+    A_ref = oracle.gdn_kkt(k, g, beta, Hv)
+    A_gpu = A.cpu().double().numpy()
+    n_rows = np.arange(T) % 64
+    valid = np.arange(64)[None, :] <= (np.minimum(64, T - (np.arange(T) // 64) * 64) - 1)[:, None]
+    diff = np.abs(A_gpu - A_ref)[:, :, :, :] * valid[None, :, None, :]
+    a_err = diff.max() / max(1.0, np.abs(A_ref).max())
+    print(f"A: max rel err {a_err:.3e} (tol {A_TOL[dtype]:.1e})", flush=True)
+    assert a_err <= A_TOL[dtype]
+    # the chunk recurrence on the GPU's A
+    A_used = A_gpu * valid[None, :, None, :]
+    ro, rs = oracle.gdn_chunked(q, k, v, g, beta, A_used, w.scale, s0)
+    assert np.all(np.isfinite(o.cpu().float().numpy()))
+    assert _err(o.cpu().double().numpy(), ro, "O vs chunked oracle") <= TOL
+    assert _err(sf.cpu().double().numpy(), rs, "state vs chunked oracle") <= TOL
+    # and the token recurrence with the exact A
+    to, ts = oracle.gdn_recurrent(q, k, v, g, beta, w.scale, s0)
+    assert _err(o.cpu().double().numpy(), to, "O vs token recurrence") <= 2 * TOL
+    assert _err(sf.cpu().double().numpy(), ts, "state vs token recurrence") <= 2 * TOL
+
+
+def test_gdn_deterministic():
+    w, (q, k, v, g, beta, s0) = _case(1, 300, 2, 4, 128, torch.bfloat16, True, seed=11)
+    dev = [t.cuda() for t in (q, k, v, g, beta, s0)]
+    a = fa.gdn_prefill(*dev[:5], s0=dev[5])
+    b = fa.gdn_prefill(*dev[:5], s0=dev[5])
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", list(GDN_WORKLOADS))
+def test_gdn_workload_sampled(name):
+    """The benchmark workloads at full size: the first and last value heads' outputs over the first
+    512 tokens against the oracle run on that prefix (the recurrence is causal), and every state
+    finite."""
+    w = GDN_WORKLOADS[name]
+    q, k, v, g, beta, s0 = make_gdn_inputs(w)
+    dev = [t.cuda() if t is not None else None for t in (q, k, v, g, beta, s0)]
+    o, sf, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sf).all() and torch.isfinite(o.float()).all()
+    P = 512
+    sl = lambda t: t[:1, :P].contiguous() if t is not None else None  # noqa: E731
+    qp, kp, vp, gp, bp = (sl(t) for t in (q, k, v, g, beta))
+    s0p = s0[:1].contiguous() if s0 is not None else None
+    ro, _ = oracle.gdn_chunked(qp, kp, vp, gp, bp, A[:1, :P].cpu().double().numpy(), w.scale, s0p)
+    og = o[:1, :P].cpu().double().numpy()
+    assert _err(og, ro, f"{name} O, first {P} tokens of batch 0") <= TOL
