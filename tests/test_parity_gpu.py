@@ -58,6 +58,12 @@ SMALL = [
     (4, 64, 64, 260, 130, 64, False, torch.float16),
     (2, 128, 16, 513, 700, 128, True, torch.float16),
     (1, 256, 32, 256, 64, 64, True, torch.bfloat16),      # exactly one key tile per row
+    # more ragged small grids
+    (5, 20, 4, 300, 400, 128, True, torch.float16),
+    (1, 4, 2, 200, 200, 128, True, torch.bfloat16),
+    (1, 2, 2, 100, 333, 64, False, torch.float16),
+    (1, 2, 1, 64, 130, 128, False, torch.bfloat16),
+    (1, 3, 1, 400, 100, 128, True, torch.float16),       # M > N: whole query tiles with no key
 ]
 
 
