@@ -57,9 +57,19 @@ __host__ __device__ constexpr int pi32_inv(int k) { return ((k & 15) >> 2) * 8 +
 //     them over all 16 bank groups.
 //   V tile: row-major in key order; a transposing pass reads 4 consecutive rows x 4 units, so
 //     the pitch shifts consecutive rows by 4 bank groups.
+//   At D = 128 the rows are instead exactly 256 bytes (one pass over the 64 banks) and the
+//   16-byte units are XOR-swizzled, which is conflict-free for the same passes without pad
+//   bytes: no pad lanes in the tile copies and 16 whole 1 KiB copy instructions per tile.
+//   K: unit u of slot r at u ^ (4 (r mod 4) + (r / 4) mod 4), which spreads the 16 slots of a
+//   read pass over all 16 bank groups; V: unit u of row r at u ^ 4 (r mod 4), which spreads the
+//   4 rows x 4 units of a transposing pass.  A read address is then a per-lane offset chosen by
+//   the k-step (K) or column block (V) plus a compile-time row offset.
 template <int D> struct Lds {
-    static constexpr int K_PITCH = D == 128 ? 17 * 16 : 9 * 16;   // bytes
-    static constexpr int V_PITCH = D == 128 ? 20 * 16 : 12 * 16;  // bytes
+    static constexpr bool SWZ = D == 128;
+    static constexpr int K_PITCH = D == 128 ? 16 * 16 : 9 * 16;   // bytes
+    static constexpr int V_PITCH = D == 128 ? 16 * 16 : 12 * 16;  // bytes
+    static __device__ __forceinline__ constexpr int k_swz(int r) { return SWZ ? 4 * (r & 3) + ((r >> 2) & 3) : 0; }
+    static __device__ __forceinline__ constexpr int v_swz(int r) { return SWZ ? 4 * (r & 3) : 0; }
 };
 
 struct Params {
@@ -111,6 +121,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     constexpr int KB = kBN / 32;                       // 32-key blocks per tile
     constexpr int DB = D / 32;                         // 32-column blocks of the output
     constexpr int KP = Lds<D>::K_PITCH, VP = Lds<D>::V_PITCH;
+    constexpr bool SWZ = Lds<D>::SWZ;
     constexpr int K_TILE = kBN * KP, V_TILE = kBN * VP;
 
     // [K buf 0 .. NBUF-1 | V buf 0 .. NBUF-1 | 1 KiB sink for padding loads]
@@ -206,15 +217,15 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
         const int u = (wave_u + kWaves * i) * 64 + lane;  // 16-byte unit of the K tile this lane fills
-        const int slot = u / (KP / 16), unit = u % (KP / 16);
+        const int slot = u / (KP / 16), unit = u % (KP / 16);  // LDS slot and physical unit
         const int key = (slot & ~31) | pi32(slot & 31);    // slot order pi inside each 32-key block
-        k_src[i] = unit < UNITS && u < K_INSTR * 64 ? (unsigned)(key * k_rs + unit * 16) : kPad;
+        k_src[i] = unit < UNITS && u < K_INSTR * 64 ? (unsigned)(key * k_rs + (unit ^ Lds<D>::k_swz(slot)) * 16) : kPad;
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
         const int u = (wave_u + kWaves * i) * 64 + lane;
         const int row = u / (VP / 16), unit = u % (VP / 16);
-        v_src[i] = unit < UNITS && u < V_INSTR * 64 ? (unsigned)(row * v_rs + unit * 16) : kPad;
+        v_src[i] = unit < UNITS && u < V_INSTR * 64 ? (unsigned)(row * v_rs + (unit ^ Lds<D>::v_swz(row)) * 16) : kPad;
     }
     // buffer resource of key tile t: its rows up to kv_end, so a row past it (every byte of which
     // lies at or beyond (rows - 1) * row_bytes + D * sizeof(T)) reads as zero
@@ -264,12 +275,22 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     const int causal_lim = qpos + (N - M);  // last visible key of this row (causal)
 
     // per-lane read bases: K slot ql of each 32-key block, unit hh of each 32-byte k-step
-    const int k_rd = ql * KP + hh * 16;
+    const int k_rd = SWZ ? 0 : ql * KP + hh * 16;
     // transposing V read: in each 16-lane group, source lane 4*e + j reads row (4-row group base + e)
     // at column chunk dcol(j); the result gives lane l the 4 keys of column pi(l % 32)
     const int tr_g = (lane >> 4) & 1, tr_s = lane & 15, tr_e = tr_s >> 2, tr_j = tr_s & 3;
     const int tr_dcol = 16 * (tr_j & 1) + 8 * tr_g + 4 * (tr_j >> 1);
-    const int v_rd = (hh * 16 + tr_e) * VP + tr_dcol * 2;
+    const int v_rd = SWZ ? 0 : (hh * 16 + tr_e) * VP + tr_dcol * 2;
+    // swizzled tiles: per-lane offsets of K k-step ks (slot ql, unit 2 ks + hh) and of the V column
+    // block db (row 16 hh + tr_e; the swizzle only flips the block bits, by tr_e)
+    unsigned koff[SWZ ? KS : 1], voff[SWZ ? DB : 1];
+    if constexpr (SWZ) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) koff[ks] = (unsigned)(ql * KP + (((2 * ks + hh) ^ Lds<D>::k_swz(ql)) * 16));
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            voff[db] = (unsigned)((hh * 16 + tr_e) * VP + (4 * (db ^ tr_e) + 2 * (tr_j & 1) + tr_g) * 16 + 8 * (tr_j >> 1));
+    }
 
     // ---- A5: visibility of key `key` to this lane's row (diagonal band / ragged last tile)
     auto visible = [&](int key) { return key < N && (!CAUSAL || key <= causal_lim); };
@@ -330,9 +351,13 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     // LDS operand of MFMA j: a K fragment (j < NM) or two transposing V reads (j >= NM).
     // Value MFMA i = j - NM: key block kb = i / (2 DB), key octet tt = (i / DB) % 2, column block i % DB.
     auto read_op = [&](int j, const lds_u8 *kp, const lds_u8 *vp) {
-        if (j < NM) return *(const lds_u32x4 *)(kp + (j % KB) * 32 * KP + (j / KB) * 32);
+        if (j < NM) {
+            if constexpr (SWZ) return *(const lds_u32x4 *)(kp + koff[j / KB] + (j % KB) * 32 * KP);
+            return *(const lds_u32x4 *)(kp + (j % KB) * 32 * KP + (j / KB) * 32);
+        }
         const int i = j - NM, kb = i / (2 * DB), tt = (i / DB) % 2, db = i % DB;
-        const int off = (kb * 32 + tt * 8) * VP + db * 64;  // rows k0.., columns of block db
+        // rows k0.., columns of block db
+        const int off = SWZ ? (kb * 32 + tt * 8) * VP + (int)voff[SWZ ? db : 0] : (kb * 32 + tt * 8) * VP + db * 64;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + off));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + off + 4 * VP));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
