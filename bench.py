@@ -244,11 +244,17 @@ def cpu_baseline(w, q, k, v, target_s):
     fixed = max(t1 - f1 * per_flop, 0.0)
     avg_row = accounting.causal_adjusted_flops(1, 1, w.M, w.N, w.D, w.causal) / w.M
     n = int(min(total_rows, max(256, (target_s - fixed) / per_flop / avg_row)))
-    rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.attn_fwd_rows(qc, kc, vc, w.scale, w.causal, rows)
-    dt = time.perf_counter() - t0
-    fl = flops_of(rows)
+    # the probes run below full thread efficiency, so a first sample can come out short: one
+    # resize from its own measured rate
+    for attempt in range(2):
+        rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attn_fwd_rows(qc, kc, vc, w.scale, w.causal, rows)
+        dt = time.perf_counter() - t0
+        fl = flops_of(rows)
+        if dt >= 0.6 * target_s or n == total_rows or attempt == 1:
+            break
+        n = int(min(total_rows, n * target_s / max(dt, 1e-3)))
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOPS",
