@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
     lds_u8 *st = smem + OFF_ST, *wt = smem + OFF_WT, *sc = smem + OFF_SC, *vn = smem + OFF_VN,
            *vh = smem + OFF_VH;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ql = lane & 31, hh = lane >> 5;
     const int tb = wave >> 1, cb = wave & 1;  // this wave's 32x32 output block of the chunk products
     const int dvblk = (int)(blockIdx.x % p.dv_blocks);
@@ -225,13 +225,13 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         }
     };
     // V of this wave's block: column dv0 + 32 cb + ql, rows 32 tb + 8 q + 4 hh + e
-    auto load_v = [&](int c, unsigned short (&vr)[16]) {
+    auto load_v = [&](int c, unsigned (&vr)[16]) {
         const int t0 = c * C;
         const unsigned short *vb = (const unsigned short *)p.v;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int t = t0 + 32 * tb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            vr[r] = t < T_ ? vb[(((size_t)b * T_ + t) * Hv + h) * DV + dv0 + 32 * cb + ql] : (unsigned short)0;
+            vr[r] = t < T_ ? (unsigned)vb[(((size_t)b * T_ + t) * Hv + h) * DV + dv0 + 32 * cb + ql] : 0u;
         }
     };
 
@@ -273,7 +273,9 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
 
     const TrOffsets<DK> tro(lane);
     const float scale = p.scale;
-    unsigned short vcur[16], vnext[16];
+    // one element per register: packing pairs right after the loads would make the wave wait
+    // for them (and for the tile copies issued before them) before any of the chunk's work
+    unsigned vcur[16], vnext[16];
     issue(0, 0);
     load_v(0, vcur);
     write_st();
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * q + e;
                 const float eg = exp_(g4[e]);
-                const f32x2 vv = Elem<T>::unpack2((unsigned)vcur[r]);
+                const f32x2 vv = Elem<T>::unpack2(vcur[r]);
                 w[e] = b4[e] * (vv[0] - eg * U[r]);
                 // scores[t][s] for t = column, s = row: causal and gate-decayed
                 s4[e] = r0 + e <= 32 * cb + ql ? KQ[r] * exp_(g_col - g4[e]) : 0.f;
