@@ -1,8 +1,10 @@
 """MI355X (gfx950) fused attention forward: a thin Python binding over libfa.so.
 
-Every step of the computation runs in the HIP kernels of ``csrc/fa_fwd.hip``; this module
-only marshals arguments through the C ABI declared in ``include/fa.h``.  There is no
-fallback: if ``libfa.so`` is missing or cannot be loaded, every call raises.
+Every step of the computation runs in the HIP kernels of ``csrc/fa_fwd.hip`` (forward and
+key-split forward), ``csrc/fa_bwd.hip`` (backward) and ``csrc/gdn_fwd.hip`` (Gated DeltaNet
+chunked prefill); this module only marshals arguments through the C ABI declared in
+``include/fa.h`` and ``include/gdn.h``.  There is no fallback: if ``libfa.so`` is missing or
+cannot be loaded, every call raises.
 
 Functions with the C ABI's names take raw device pointers and sizes:
 
@@ -12,9 +14,13 @@ Functions with the C ABI's names take raw device pointers and sizes:
     fa_fwd_splitkv_strided(..., D, q_strides, ..., o_strides, scale, ..., workspace_bytes, stream)
     fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles_per_split)
     fa_strerror(code), fa_tile_shape(B, Hq, M, D), fa_tile_counts(...), fa_schedule(...)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, M, N, D, scale, causal, dtype, ws, ws_bytes, stream)
+    fa_bwd_workspace_size(B, Hq, M)
+    gdn_kkt(k, g, beta, A, B, T, Hqk, Hv, DK, dtype, stream)
+    gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, stream)
 
-and ``attention_forward(q, k, v, causal, scale, split_kv)`` is the torch-tensor convenience
-wrapper (torch is used only for device memory, the split workspace and the current stream).
+``attention_forward``, ``attention_backward`` and ``gdn_prefill`` are the torch-tensor
+convenience wrappers (torch is used only for device memory, workspaces and the current stream).
 """
 from __future__ import annotations
 
