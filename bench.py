@@ -15,7 +15,9 @@ K rows scaled by 8).  Prints ONE JSON line on stdout:
   cpu_baseline  the fp64 CPU oracle timed on a bounded random sample of the same workload's
             rows, in the same unit
 
-``--all`` also prints one line per workload to stderr (not part of the contract).
+``--all`` also prints one line per workload to stderr (not part of the contract); for the two
+small, cache-resident workloads the line adds a cold-cache median (a 512 MiB buffer is
+overwritten between calls) and the oracle's rate on one core.
 ``--calibrate-copy BYTES`` runs only a plain device-to-device copy of BYTES bytes (used to
 scale the FETCH_SIZE / WRITE_SIZE counters of the profiles).
 """
@@ -97,6 +99,10 @@ def roofline(w, flops, avg_ms, traffic):
             "frac": round(achieved / peak, 4), "traffic": traffic, "kernel_avg_us": round(avg_ms * 1e3, 3)}
 
 
+# workloads whose inputs fit in the 256 MB last-level cache (the small parity shapes)
+SMALL_CACHE_RESIDENT = ("tiny_causal_gqa", "pages_causal_gqa_1k")
+
+
 def time_gpu(fa, w, q, k, v, steps, warmup, split_kv="auto"):
     import torch
 
@@ -117,6 +123,57 @@ def time_gpu(fa, w, q, k, v, steps, warmup, split_kv="auto"):
     wall = time.perf_counter() - t0
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
     return wall, durs, o, lse
+
+
+def time_gpu_cold(fa, w, q, k, v, steps, split_kv="auto", flush_bytes=512 << 20):
+    """Per-call kernel times (ms, sorted) with the on-package caches flushed before every call:
+    a 512 MiB buffer is overwritten between calls, outside the timed events."""
+    import torch
+
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.M), dtype=torch.float32, device=q.device)
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, split_kv=split_kv)
+    for i in range(steps):
+        scratch.fill_(i % 251 + 1)
+        starts[i].record(stream)
+        fa.attention_forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, split_kv=split_kv)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    del scratch
+    return sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
+
+
+def oracle_one_thread(w, q, k, v, target_s=3.0):
+    """The oracle on one thread over a row sample of about target_s seconds (all rows when
+    they fit): the single-core reference point for the small workloads."""
+    import numpy as np
+
+    import oracle
+
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    total_rows = w.B * w.Hq * w.M
+    vis = (lambda i: np.clip(i + 1 + (w.N - w.M), 0, w.N)) if w.causal else (lambda i: np.full(i.shape, w.N))
+    prev = oracle.set_threads(1)
+    try:
+        rng = np.random.default_rng(4321)
+        n = min(total_rows, 256)
+        for attempt in range(3):
+            rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+            t0 = time.perf_counter()
+            oracle.attn_fwd_rows(qc, kc, vc, w.scale, w.causal, rows)
+            dt = time.perf_counter() - t0
+            if n == total_rows or dt >= 0.5 * target_s or attempt == 2:
+                break
+            n = int(min(total_rows, n * target_s / max(dt, 1e-3)))
+    finally:
+        oracle.set_threads(prev)
+    fl = float(4 * w.D * vis(rows % w.M).sum())
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {total_rows} query rows, {fl / 1e9:.3f} GFLOP in {dt:.2f} s, fp64"}
 
 
 def time_gpu_bwd(fa, w, q, k, v, steps, warmup):
@@ -342,6 +399,13 @@ def main():
             "issued_mfma_tflops": round(issued / (avg_ms * 1e-3) / 1e12, 2),
             "compulsory_gbs": round(accounting.workload_bytes(w) / (avg_ms * 1e-3) / 1e9, 1),
         }
+        if args.all and args.which == "fwd" and name in SMALL_CACHE_RESIDENT:
+            # these working sets fit in the on-package caches: also a cold-cache time, and the
+            # oracle on one core
+            cold = time_gpu_cold(fa, w, q, k, v, args.steps, split_kv)
+            line["kernel_cold_median_us"] = round(cold[len(cold) // 2] * 1e3, 2)
+            if not args.no_cpu_baseline:
+                line["oracle_1thread"] = oracle_one_thread(w, q, k, v)
         print(json.dumps(line), file=sys.stderr, flush=True)
         if name == args.workload:
             assert torch.isfinite(o.float()).all().item(), "non-finite output"

@@ -58,6 +58,8 @@ def _load():
         lib.oracle_attn_fwd_stepnorm.argtypes = [u16p, u16p, u16p] + shape + [cl, dp, dp]
         lib.oracle_attn_probs.argtypes = [u16p, u16p] + shape + [ci, ci, dp]
         lib.oracle_attn_bwd.argtypes = [u16p, u16p, u16p, u16p] + shape + [dp, dp, dp]
+        lib.oracle_set_threads.argtypes = [ci]
+        lib.oracle_set_threads.restype = ci
         lib.oracle_attn_bwd.restype = ci
         gshape = [ci, ci, ci, ci, ci, ci, ci, cd]  # B, T, Hqk, Hv, DK, DV, C, scale
         lib.oracle_gdn_recurrent.argtypes = [u16p, u16p, u16p, ci, dp, dp, dp] + gshape + [dp, dp]
@@ -278,8 +280,24 @@ def decode_array(bits: np.ndarray, dtype: int) -> np.ndarray:
     return np.array([f(int(b)) for b in bits.ravel()], dtype=np.float64).reshape(bits.shape)
 
 
+_threads_override = None
+
+
+def set_threads(n: int) -> int:
+    """Threads for later oracle calls; returns the previous count (for restoring it)."""
+    global _threads_override
+    prev = threads_used()
+    lib = _load()
+    lib.oracle_set_threads(int(n))
+    _threads_override = int(n)
+    return prev
+
+
 def threads_used() -> int:
-    """OpenMP threads the oracle will use (OMP_NUM_THREADS or the process's CPU affinity)."""
+    """OpenMP threads the oracle will use (set_threads, else OMP_NUM_THREADS or the process's
+    CPU affinity)."""
+    if _threads_override is not None:
+        return _threads_override
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit() and int(env) > 0:
         return int(env)

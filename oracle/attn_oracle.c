@@ -46,6 +46,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ---------------------------------------------------------------- decoders */
 
@@ -531,4 +534,18 @@ int oracle_attn_bwd(const uint16_t *q16, const uint16_t *k16, const uint16_t *v1
     free(v);
     free(dO);
     return err ? -1 : 0;
+}
+
+/* Threads for the OpenMP loops of later calls (n >= 1; n <= 0 leaves it unchanged).  Returns
+ * the previous setting, so a caller can time a single-threaded run and restore it. */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    const int old = omp_get_max_threads();
+    if (n >= 1) omp_set_num_threads(n);
+    return old;
+#else
+    (void)n;
+    return 1;
+#endif
 }

@@ -24,8 +24,8 @@ def build(verbose: bool = False) -> str:
 
 
 def ensure_built() -> str:
-    """Build only when the library is missing."""
-    if not os.path.exists(LIB):
+    """Build when the library is missing or older than one of its sources."""
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(os.path.getmtime(f) for f in SRCS):
         build()
     return LIB
 

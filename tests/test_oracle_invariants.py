@@ -199,3 +199,17 @@ def test_scale_enters_the_logits():
     o2, lse2 = oracle.attn_fwd((q * 2).contiguous(), k, v, 0.25, True)
     np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=1e-13)
+
+
+def test_result_does_not_depend_on_thread_count():
+    # every row is computed on its own, in index order: one thread and many give the same bits
+    q, k, v = make_custom(2, 4, 2, 37, 53, 64, torch.float16, seed=11)
+    full_o, full_lse = oracle.attn_fwd(q, k, v, 0.125, True)
+    prev = oracle.set_threads(1)
+    try:
+        assert oracle.threads_used() == 1
+        one_o, one_lse = oracle.attn_fwd(q, k, v, 0.125, True)
+    finally:
+        oracle.set_threads(prev)
+    assert oracle.threads_used() == prev
+    assert np.array_equal(full_o, one_o) and np.array_equal(full_lse, one_lse)
