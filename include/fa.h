@@ -27,6 +27,12 @@
  *     j <= i + (N - M) (the pages' "i >= j" when M == N);
  *   - a query row that sees no key (causal, M > N) gets O = 0 and lse = -inf;
  *   - lse is the natural log over the *scaled* logits.
+ *
+ * Every entry point below (and those of gdn.h) validates its arguments on the host, then only
+ * enqueues kernels on the caller's stream: it never allocates, frees, memsets or
+ * synchronises, and keeps no state between calls.  Calls are therefore safe from several host
+ * threads at once and can be captured into a HIP graph (stream capture); outputs and
+ * workspaces keep the addresses the captured call was given.
  */
 #ifndef FA_H
 #define FA_H
