@@ -57,6 +57,8 @@ def _parse():
                     help="time the forward, or the backward (dq, dk, dv from a forward's O and lse)")
     ap.add_argument("--layout", choices=["bhsd", "bshd"], default="bhsd",
                     help="memory layout of q, k, v, o: contiguous [B,H,S,D] or [B,S,H,D] buffers (strided path)")
+    ap.add_argument("--gdn-mode", choices=["auto", "one", "two"], default="auto",
+                    help="Gated DeltaNet workloads: the library's pick, the one-kernel or the two-kernel mode")
     ap.add_argument("--split-kv", default="auto",
                     help="'auto' (key-split forward for small grids), 'off', or key tiles per share")
     return ap.parse_args()
@@ -217,11 +219,14 @@ def run_gdn(args, fa, w):
     sf = torch.empty((B, Hv, DK, DV), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     dt = 0 if q.dtype == torch.float16 else 1
+    ws_bytes = {"auto": lambda: fa.gdn_chunk_plan(B, T, Hv, DV), "one": lambda: 0,
+                "two": lambda: fa.gdn_chunk_workspace_size(B, T, Hv, DV)}[args.gdn_mode]()
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def call():
         rc = fa.gdn_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), A.data_ptr(),
                               s0.data_ptr() if s0 is not None else None, o.data_ptr(), sf.data_ptr(), B, T, Hqk, Hv,
-                              DK, DV, w.scale, dt, stream.cuda_stream)
+                              DK, DV, w.scale, dt, ws.data_ptr() if ws_bytes else None, ws_bytes, stream.cuda_stream)
         assert rc == 0, rc
 
     for _ in range(args.warmup):
@@ -241,7 +246,8 @@ def run_gdn(args, fa, w):
     flops = accounting.gdn_flops(B, T, Hv, DK, DV)
     nbytes = accounting.gdn_bytes(B, T, Hqk, Hv, DK, DV, s0 is not None)
     assert torch.isfinite(sf).all().item(), "non-finite state"
-    line = {"workload": w.name, "path": "gdn_chunk_fwd", "ms": round(avg_ms, 4),
+    path = "gdn_chunk_fwd (state walk + parallel outputs)" if ws_bytes else "gdn_chunk_fwd (one kernel)"
+    line = {"workload": w.name, "path": path, "ms": round(avg_ms, 4),
             "median_ms": round(durs[len(durs) // 2], 4), "tflops": round(flops / (avg_ms * 1e-3) / 1e12, 2),
             "compulsory_gbs": round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
             "workgroups": B * Hv * (DV // 64)}

@@ -17,7 +17,8 @@ Functions with the C ABI's names take raw device pointers and sizes:
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, M, N, D, scale, causal, dtype, ws, ws_bytes, stream)
     fa_bwd_workspace_size(B, Hq, M)
     gdn_kkt(k, g, beta, A, B, T, Hqk, Hv, DK, dtype, stream)
-    gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, stream)
+    gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, ws, ws_bytes, stream)
+    gdn_chunk_workspace_size(B, T, Hv, DV), gdn_chunk_plan(B, T, Hv, DV)
 
 ``attention_forward``, ``attention_backward`` and ``gdn_prefill`` are the torch-tensor
 convenience wrappers (torch is used only for device memory, workspaces and the current stream).
@@ -86,8 +87,12 @@ def _load():
     fp = ctypes.POINTER(ctypes.c_float)
     lib.gdn_kkt.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
     lib.gdn_kkt.restype = ci
-    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp, sz, vp]
     lib.gdn_chunk_fwd.restype = ci
+    lib.gdn_chunk_workspace_size.argtypes = [ci, ci, ci, ci]
+    lib.gdn_chunk_workspace_size.restype = sz
+    lib.gdn_chunk_plan.argtypes = [ci, ci, ci, ci, ctypes.POINTER(sz)]
+    lib.gdn_chunk_plan.restype = ci
     _lib = lib
     return lib
 
@@ -161,10 +166,26 @@ def gdn_kkt(k, g, beta, A, B, T, Hqk, Hv, DK, dtype, stream) -> int:
     return _load().gdn_kkt(k, g, beta, A, B, T, Hqk, Hv, DK, int(dtype), stream)
 
 
-def gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, stream) -> int:
-    """Raw C ABI call (include/gdn.h): the Gated DeltaNet chunk recurrence."""
+def gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, workspace,
+                  workspace_bytes, stream) -> int:
+    """Raw C ABI call (include/gdn.h): the Gated DeltaNet chunk recurrence (workspace None: the
+    one-kernel mode; else the state walk plus the parallel output kernel)."""
     return _load().gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, float(scale), int(dtype),
-                                 stream)
+                                 workspace, int(workspace_bytes), stream)
+
+
+def gdn_chunk_workspace_size(B: int, T: int, Hv: int, DV: int) -> int:
+    """Bytes of the gdn_chunk_fwd workspace of the two-kernel mode."""
+    return int(_load().gdn_chunk_workspace_size(B, T, Hv, DV))
+
+
+def gdn_chunk_plan(B: int, T: int, Hv: int, DV: int) -> int:
+    """Workspace bytes of the mode the library picks for this shape (0: the one-kernel mode)."""
+    ws = ctypes.c_size_t()
+    rc = _load().gdn_chunk_plan(B, T, Hv, DV, ctypes.byref(ws))
+    if rc != FA_OK:
+        raise FaError(rc, "gdn_chunk_plan")
+    return int(ws.value)
 
 
 def fa_strerror(code: int) -> str:
@@ -307,10 +328,13 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     return dq, dk, dv
 
 
-def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, stream=None):
+def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, stream=None, two_kernel="auto"):
     """Gated DeltaNet chunked prefill on contiguous device tensors: q, k [B,T,Hqk,128], v [B,T,Hv,DV]
     (fp16/bf16), g and beta [B,T,Hv] fp32 (g: cumulative log-gate inside each 64-token chunk),
     s0 [B,Hv,128,DV] fp32 or None.  A [B,T,Hv,64] (dtype) is computed with gdn_kkt when not given.
+    two_kernel: True for the state walk plus the parallel output kernel (workspace from torch's
+    caching allocator), False for the one-kernel mode, "auto" for the library's pick
+    (gdn_chunk_plan); all give the same bits.
     Returns (o [B,T,Hv,DV], final state [B,Hv,128,DV] fp32, A)."""
     import torch
 
@@ -335,13 +359,20 @@ def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, s
             raise FaError(rc, "gdn_kkt")
     o = torch.empty((B, T, Hv, DV), dtype=q.dtype, device=q.device)
     sf = torch.empty((B, Hv, DK, DV), dtype=torch.float32, device=q.device)
+    ws, ws_bytes = None, 0
+    if two_kernel == "auto":
+        ws_bytes = gdn_chunk_plan(B, T, Hv, DV)
+    elif two_kernel:
+        ws_bytes = gdn_chunk_workspace_size(B, T, Hv, DV)
+    if ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     rc = gdn_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), A.data_ptr(),
                        s0.data_ptr() if s0 is not None else None, o.data_ptr(), sf.data_ptr(), B, T, Hqk, Hv, DK, DV,
-                       scale, dt, stream)
+                       scale, dt, ws.data_ptr() if ws is not None else None, ws_bytes, stream)
     if rc != FA_OK:
         raise FaError(rc, "gdn_chunk_fwd")
     return o, sf, A
 
 
-__all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_prefill", "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+__all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_chunk_plan", "gdn_prefill", "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]

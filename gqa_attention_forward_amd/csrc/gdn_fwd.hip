@@ -158,11 +158,18 @@ struct ChunkParams {
     const float *s0;  // may be null
     void *o;
     float *s_final;
+    // two-kernel mode: the state at each chunk start, [B*Hv][chunks][DV][DK] (dtype), and
+    // V_new, [B*Hv][chunks][DV][64] (dtype), both transposed (state column / value column major)
+    void *ws_st, *ws_vn;
     int B, T, Hqk, Hv, DV, n_chunks, dv_blocks;
     float scale;
 };
 
-template <typename T>
+// SPLIT = false: the whole chunk step (state and output) in one kernel.  SPLIT = true: only
+// the sequential part -- U', W', V_new and the state update -- stores each chunk's starting
+// state and V_new (as the dtype operands the output products use) for out_kernel, which forms
+// the outputs of all chunks in parallel.
+template <typename T, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
 {
     // LDS: two input buffers [Q | K | A | g | beta] and the per-chunk work arrays
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const unsigned off = qk_src + (unsigned)(16 * i * qk_rs);
-            lds_load16(rq, (lds_void *)(dst + (wave + 4 * i) * 1024), off);
+            if constexpr (!SPLIT) lds_load16(rq, (lds_void *)(dst + (wave + 4 * i) * 1024), off);
             lds_load16(rk, (lds_void *)(dst + QK_TILE + (wave + 4 * i) * 1024), off);
         }
         const __amdgpu_buffer_rsrc_t ra = rsrc(abase + (size_t)t0 * Hv * C, (n - 1) * a_rs + C * sizeof(T));
@@ -246,6 +253,10 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             S[j][r] = p.s0 ? p.s0[((size_t)bh * DK + d) * DV + e] : 0.f;
         }
     // bf16 copy of the state, transposed: St[column][key dim], 16 consecutive key dims per lane
+    // (two-kernel mode: the same 16-byte pieces are kept in `stash` and stored to the workspace
+    // as the chunk's starting state by store_st, once the chunk's loads have been issued, so
+    // that the wait for those loads at the end of the chunk does not also wait for the stores)
+    u32x4 stash[4];
     auto write_st = [&]() {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -258,6 +269,17 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             lds_u8 *dst = st + (32 * j + ql) * SP + (32 * wave + 16 * hh) * 2;
             *(lds_u32x4 *)dst = w0;
             *(lds_u32x4 *)(dst + 16) = w1;
+            stash[2 * j] = w0;
+            stash[2 * j + 1] = w1;
+        }
+    };
+    auto store_st = [&](int cidx) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            u32x4 *g = (u32x4 *)((T *)p.ws_st + (((size_t)bh * p.n_chunks + cidx) * DV + dv0 + 32 * j + ql) * DK +
+                                 32 * wave + 16 * hh);
+            g[0] = stash[2 * j];
+            g[1] = stash[2 * j + 1];
         }
     };
     // 8-byte transposed write: 4 accumulator rows (registers 4 q .. 4 q + 3) of column `col`
@@ -288,6 +310,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             issue(c + 1, buf ^ 1);
             load_v(c + 1, vnext);
         }
+        if constexpr (SPLIT) store_st(c);
         const lds_u8 *qt = smem + buf * BUF, *kt = qt + QK_TILE, *at = kt + QK_TILE;
         const lds_f32 *gl = (const lds_f32 *)(at + A_TILE), *bl = gl + C;
 
@@ -303,12 +326,14 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             const int u = 2 * ks + hh;
             const u32x4 sb = row16(st, SP, 32 * cb + ql, u);
             const u32x4 ka = read_row<DK>(kt, 32 * tb + ql, u);
-            const u32x4 qa = read_row<DK>(qt, 32 * tb + ql, u);
             U = Elem<T>::mfma(ka, sb, U);
-            O = Elem<T>::mfma(row16(st, SP, 32 * cb + perm32(ql), u), qa, O);
-            KQ = Elem<T>::mfma(ka, read_row<DK>(qt, 32 * cb + ql, u), KQ);
+            if constexpr (!SPLIT) {
+                const u32x4 qa = read_row<DK>(qt, 32 * tb + ql, u);
+                O = Elem<T>::mfma(row16(st, SP, 32 * cb + perm32(ql), u), qa, O);
+                KQ = Elem<T>::mfma(ka, read_row<DK>(qt, 32 * cb + ql, u), KQ);
+            }
         }
-        {
+        if constexpr (!SPLIT) {
             const float eg = exp_(gl[32 * tb + ql]);  // O^T column t = 32 tb + ql
 #pragma unroll
             for (int r = 0; r < 16; ++r) O[r] *= eg;
@@ -327,10 +352,10 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
                 const f32x2 vv = Elem<T>::unpack2(vcur[r]);
                 w[e] = b4[e] * (vv[0] - eg * U[r]);
                 // scores[t][s] for t = column, s = row: causal and gate-decayed
-                s4[e] = r0 + e <= 32 * cb + ql ? KQ[r] * exp_(g_col - g4[e]) : 0.f;
+                if constexpr (!SPLIT) s4[e] = r0 + e <= 32 * cb + ql ? KQ[r] * exp_(g_col - g4[e]) : 0.f;
             }
             put4(wt, AP, 32 * cb + ql, r0, w[0], w[1], w[2], w[3]);
-            put4(sc, AP, 32 * cb + ql, r0, s4[0], s4[1], s4[2], s4[3]);
+            if constexpr (!SPLIT) put4(sc, AP, 32 * cb + ql, r0, s4[0], s4[1], s4[2], s4[3]);
         }
         __syncthreads();
 
@@ -346,7 +371,14 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         for (int q = 0; q < 4; ++q) {
             const int r0 = 32 * tb + 8 * q + 4 * hh;
             const f32x4 g4 = *(const lds_f32x4 *)(gl + r0);
-            put4(vn, AP, 32 * cb + ql, r0, V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);
+            if constexpr (SPLIT) {  // V_new^T rows (value columns) of 64 tokens
+                u32x2 w;
+                w[0] = Elem<T>::pack2(V[4 * q], V[4 * q + 1]);
+                w[1] = Elem<T>::pack2(V[4 * q + 2], V[4 * q + 3]);
+                *(u32x2 *)((T *)p.ws_vn + (((size_t)bh * p.n_chunks + c) * DV + dv0 + 32 * cb + ql) * C + r0) = w;
+            } else {
+                put4(vn, AP, 32 * cb + ql, r0, V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);
+            }
             // decayed copy for the state update, positions with bits 2 and 3 of s swapped so that
             // the 8 rows one transposing K read pairs with are 16 contiguous bytes
             const int p0 = 32 * tb + 16 * (q >> 1) + 8 * hh + 4 * (q & 1);
@@ -356,6 +388,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         __syncthreads();
 
         // ---- O = scale (exp(g) Q S_c + scores V_new)
+        if constexpr (!SPLIT) {
 #pragma unroll
         for (int ks = 0; ks < C / 16; ++ks)
             O = Elem<T>::mfma(row16(vn, AP, 32 * cb + perm32(ql), 2 * ks + hh), row16(sc, AP, 32 * tb + ql, 2 * ks + hh),
@@ -371,6 +404,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
                                    16 * hh);
             dst[0] = w0;
             dst[1] = w1;
+        }
         }
         // ---- S_{c+1} = exp(g_last) S_c + K^T (exp(g_last - g) V_new)
         const float decay = exp_(g_last);
@@ -401,6 +435,122 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             const int d = 32 * wave + 16 * hh + r, e = dv0 + 32 * j + ql;
             p.s_final[((size_t)bh * DK + d) * DV + e] = S[j][r];
         }
+}
+
+// Outputs of the two-kernel mode: one workgroup per (b, value head, chunk, 64 value columns),
+// all independent.  With the chunk's starting state S_c and V_new from chunk_kernel<T, true>,
+//     O = scale (exp(g) (Q S_c) + scores V_new)
+// by the same products, in the same order and on the same rounded operands as the fused
+// kernel (so both modes give identical bits): O^T = S_c^T Q^T, scaled by exp(g) per token,
+// then += V_new^T scores^T.
+template <typename T>
+__global__ __launch_bounds__(256, 2) void out_kernel(ChunkParams p)
+{
+    constexpr int TILE = C * DK * 2;  // Q, K and S_c^T tiles: swizzled 256-byte rows
+    constexpr int AP = 9 * 16;        // V_new^T and scores pitch in bytes (64 elements + pad)
+    constexpr int OFF_K = TILE, OFF_S = 2 * TILE, OFF_VN = 3 * TILE, OFF_SC = OFF_VN + DVB * AP,
+                  OFF_G = OFF_SC + C * AP, SMEM = OFF_G + 256;
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM];
+    lds_u8 *smem = (lds_u8 *)smem_raw;
+    const lds_u8 *qt = smem, *kt = smem + OFF_K, *stl = smem + OFF_S, *vnl = smem + OFF_VN;
+    lds_u8 *sc = smem + OFF_SC;
+    const lds_f32 *gl = (const lds_f32 *)(smem + OFF_G);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ql = lane & 31, hh = lane >> 5;
+    const int tb = wave >> 1, cb = wave & 1;  // this wave's 32x32 output block
+    const int dvblk = (int)(blockIdx.x % p.dv_blocks);
+    const long long rest = blockIdx.x / p.dv_blocks;
+    const int c = (int)(rest % p.n_chunks);
+    const long long bh = rest / p.n_chunks;
+    const int b = (int)(bh / p.Hv), h = (int)(bh % p.Hv), hk = h / (p.Hv / p.Hqk);
+    const int dv0 = dvblk * DVB, T_ = p.T, Hv = p.Hv, DV = p.DV;
+    const int t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
+
+    // tile copies: Q, K and S_c^T (64 rows of 128 elements each, swizzled as the fused kernel's
+    // Q/K tiles), V_new^T (64 rows of 64 elements, one pad unit per row) and g (64 floats)
+    const long long qk_rs = (long long)p.Hqk * DK * sizeof(T);
+    const int row = 4 * wave + (lane >> 4), phys = lane & 15;
+    const unsigned src_qk = (unsigned)(row * qk_rs + ((phys ^ swz<DK>(row)) * 16));
+    const unsigned src_st = (unsigned)(row * (DK * (int)sizeof(T)) + ((phys ^ swz<DK>(row)) * 16));
+    const T *qb = (const T *)p.q + (((size_t)b * T_ + t0) * p.Hqk + hk) * DK;
+    const T *kb = (const T *)p.k + (((size_t)b * T_ + t0) * p.Hqk + hk) * DK;
+    const T *sb = (const T *)p.ws_st + (((size_t)bh * p.n_chunks + c) * DV + dv0) * DK;
+    const T *vb = (const T *)p.ws_vn + (((size_t)bh * p.n_chunks + c) * DV + dv0) * C;
+    const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (n - 1) * qk_rs + DK * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kb, (n - 1) * qk_rs + DK * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rs = rsrc(sb, (long long)DVB * DK * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vb, (long long)DVB * C * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // instruction j = wave + 4 i fills rows 4 j .. 4 j + 3
+        lds_load16(rq, (lds_void *)(smem + (wave + 4 * i) * 1024), src_qk + (unsigned)(16 * i * qk_rs));
+        lds_load16(rk, (lds_void *)(smem + OFF_K + (wave + 4 * i) * 1024), src_qk + (unsigned)(16 * i * qk_rs));
+        lds_load16(rs, (lds_void *)(smem + OFF_S + (wave + 4 * i) * 1024), src_st + (unsigned)(16 * i * DK * sizeof(T)));
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {  // instruction j = wave + 4 i (< 9) fills units 64 j .. 64 j + 63
+        const int u = (wave + 4 * i) * 64 + lane, r = u / 9, unit = u % 9;
+        const unsigned off = unit < 8 && r < DVB ? (unsigned)(r * C * sizeof(T) + unit * 16) : 0x7fffff00u;
+        if (wave + 4 * i < 9) lds_load16(rv, (lds_void *)(smem + OFF_VN + (wave + 4 * i) * 1024), off);
+    }
+    if (wave == 0)
+        lds_load4(rsrc(p.g + ((size_t)b * T_ + t0) * Hv + h, (long long)(n - 1) * Hv * 4 + 4),
+                  (lds_void *)(smem + OFF_G), (unsigned)(lane * Hv * 4));
+    wait_vm0();
+    __syncthreads();
+
+    auto row16 = [&](const lds_u8 *arr, int pitch, int r, int unit) {
+        return *(const lds_u32x4 *)(arr + r * pitch + unit * 16);
+    };
+    // O^T = S_c^T Q^T and K Q^T, this wave's blocks (rows of S_c^T read in perm32 order, as in
+    // the fused kernel, so that lane (t = 32 tb + ql, hh) holds 16 consecutive columns)
+    f32x16 O, KQ;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[r] = KQ[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks) {
+        const int u = 2 * ks + hh;
+        const u32x4 ka = read_row<DK>(kt, 32 * tb + ql, u);
+        const u32x4 qa = read_row<DK>(qt, 32 * tb + ql, u);
+        O = Elem<T>::mfma(read_row<DK>(stl, 32 * cb + perm32(ql), u), qa, O);
+        KQ = Elem<T>::mfma(ka, read_row<DK>(qt, 32 * cb + ql, u), KQ);
+    }
+    {
+        const float eg = exp_(gl[32 * tb + ql]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[r] *= eg;
+    }
+    // scores, transposed into LDS: rows s = 32 tb + 8 q + 4 hh + e, column t = 32 cb + ql
+    const float g_col = gl[32 * cb + ql];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r0 = 32 * tb + 8 * q + 4 * hh;
+        const f32x4 g4 = *(const lds_f32x4 *)(gl + r0);
+        float s4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            s4[e] = r0 + e <= 32 * cb + ql ? KQ[4 * q + e] * exp_(g_col - g4[e]) : 0.f;
+        u32x2 w;
+        w[0] = Elem<T>::pack2(s4[0], s4[1]);
+        w[1] = Elem<T>::pack2(s4[2], s4[3]);
+        *(__attribute__((address_space(3))) u32x2 *)(sc + (32 * cb + ql) * AP + r0 * 2) = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < C / 16; ++ks)
+        O = Elem<T>::mfma(row16(vnl, AP, 32 * cb + perm32(ql), 2 * ks + hh), row16(sc, AP, 32 * tb + ql, 2 * ks + hh), O);
+    if (32 * tb + ql < n) {
+        const float scale = p.scale;
+        u32x4 w0, w1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            w0[r] = Elem<T>::pack2(O[2 * r] * scale, O[2 * r + 1] * scale);
+            w1[r] = Elem<T>::pack2(O[8 + 2 * r] * scale, O[8 + 2 * r + 1] * scale);
+        }
+        u32x4 *dst = (u32x4 *)((T *)p.o + (((size_t)b * T_ + t0 + 32 * tb + ql) * Hv + h) * DV + dv0 + 32 * cb + 16 * hh);
+        dst[0] = w0;
+        dst[1] = w1;
+    }
 }
 
 }  // namespace gdn
@@ -435,9 +585,37 @@ int gdn_kkt(const void *k, const float *g, const float *beta, void *A, int B, in
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// bytes of the two-kernel workspace: the chunk states (256-byte aligned end), then V_new
+static size_t ws_states_bytes(int B, int T, int Hv, int DV)
+{
+    const size_t chunks = (size_t)B * Hv * ((T + fa::gdn::C - 1) / fa::gdn::C);
+    return (chunks * DV * fa::gdn::DK * 2 + 255) & ~(size_t)255;
+}
+
+size_t gdn_chunk_workspace_size(int B, int T, int Hv, int DV)
+{
+    if (B <= 0 || T <= 0 || Hv <= 0 || DV <= 0) return 0;
+    const size_t chunks = (size_t)B * Hv * ((T + fa::gdn::C - 1) / fa::gdn::C);
+    return ws_states_bytes(B, T, Hv, DV) + chunks * DV * fa::gdn::C * 2;
+}
+
+// The two-kernel mode pays for a round trip of every chunk's state and V_new through HBM and
+// an extra launch, and gains a shorter sequential step; it wins when the state walk leaves most
+// CUs idle.  Rule: state-walk workgroups (B * Hv * DV / 64) at most half the 256 CUs.
+int gdn_chunk_plan(int B, int T, int Hv, int DV, size_t *workspace_bytes)
+{
+    if (!workspace_bytes) return FA_ERR_INVALID_ARG;
+    *workspace_bytes = 0;
+    if (B <= 0 || T <= 0 || Hv <= 0 || DV <= 0) return FA_ERR_INVALID_ARG;
+    if (DV % fa::gdn::DVB != 0) return FA_ERR_UNSUPPORTED;
+    const long long walkers = (long long)B * Hv * (DV / fa::gdn::DVB);
+    if (walkers <= 128) *workspace_bytes = gdn_chunk_workspace_size(B, T, Hv, DV);
+    return FA_OK;
+}
+
 int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *A,
                   const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv, int DK, int DV, float scale,
-                  int dtype, void *stream)
+                  int dtype, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!q || !k || !v || !g || !beta || !A || !o || !s_final) return FA_ERR_INVALID_ARG;
     if (B <= 0 || T <= 0 || Hqk <= 0 || Hv <= 0 || DK <= 0 || DV <= 0 || Hv % Hqk != 0) return FA_ERR_INVALID_ARG;
@@ -446,6 +624,10 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)A | (uintptr_t)o |
                          (uintptr_t)s_final | (uintptr_t)s0 | (uintptr_t)g | (uintptr_t)beta;
     if (al & 15u) return FA_ERR_UNSUPPORTED;
+    if (workspace) {
+        if (workspace_bytes < gdn_chunk_workspace_size(B, T, Hv, DV)) return FA_ERR_INVALID_ARG;
+        if ((uintptr_t)workspace & 255u) return FA_ERR_UNSUPPORTED;
+    }
     // tile copies use 32-bit offsets inside one chunk: 63 rows of q/k, A, g and beta
     if ((long long)Hqk * fa::gdn::DK * 2 * 64 > 0x7fff0000LL || (long long)Hv * 64 * 2 * 64 > 0x7fff0000LL)
         return FA_ERR_UNSUPPORTED;
@@ -467,13 +649,28 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     p.n_chunks = (T + fa::gdn::C - 1) / fa::gdn::C;
     p.dv_blocks = DV / fa::gdn::DVB;
     p.scale = scale;
+    p.ws_st = workspace;
+    p.ws_vn = workspace ? (void *)((char *)workspace + ws_states_bytes(B, T, Hv, DV)) : nullptr;
     const long long grid = (long long)B * Hv * p.dv_blocks;
-    if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    const long long grid_out = grid * p.n_chunks;
+    if (grid_out > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
+    if (!workspace) {
+        if (dtype == FA_F16)
+            hipLaunchKernelGGL((fa::gdn::chunk_kernel<_Float16, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((fa::gdn::chunk_kernel<__bf16, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
     if (dtype == FA_F16)
-        hipLaunchKernelGGL((fa::gdn::chunk_kernel<_Float16>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((fa::gdn::chunk_kernel<_Float16, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((fa::gdn::chunk_kernel<__bf16>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((fa::gdn::chunk_kernel<__bf16, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    if (dtype == FA_F16)
+        hipLaunchKernelGGL((fa::gdn::out_kernel<_Float16>), dim3((unsigned)grid_out), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((fa::gdn::out_kernel<__bf16>), dim3((unsigned)grid_out), dim3(256), 0, s, p);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

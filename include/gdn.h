@@ -29,16 +29,33 @@
  *
  * gdn_kkt: computes A from k, g, beta (K K^T in fp32 on MFMA, the inverse by forward
  *   substitution in fp32, rounded to dtype once).  One kernel on `stream`.
- * gdn_chunk_fwd: the chunk recurrence; one kernel on `stream`, one workgroup per (b, value head,
- *   64 state columns) walking the chunks in order.  Operands of the products are rounded to
- *   dtype (the state's operand copy included); accumulation and the state itself are fp32.
+ * gdn_chunk_fwd: the chunk recurrence.  Operands of the products are rounded to dtype (the
+ *   state's operand copy included); accumulation and the state itself are fp32.  Two modes,
+ *   with bit-identical results:
+ *   - workspace == NULL: one kernel, one workgroup per (b, value head, 64 state columns)
+ *     walking the chunks in order and forming each chunk's output on the way;
+ *   - workspace != NULL: the page's own split of the work into a sequential state path and an
+ *     output path that only reads the state, taken further: one kernel walks the chunks doing
+ *     only U', W', V_new and the state update, storing each chunk's starting state and V_new
+ *     (dtype) in the workspace; a second kernel then forms all chunks' outputs in parallel.
+ *     `workspace` is DEVICE memory owned by the caller, 256-byte aligned, at least
+ *     gdn_chunk_workspace_size(B, T, Hv, DV) bytes (`workspace_bytes` its size), and must not
+ *     be in use by another call at the same time; its contents on entry do not matter.
+ *   gdn_chunk_workspace_size returns that size (0 for a non-positive argument).
+ * gdn_chunk_plan: the mode this library would pick for the shape: *workspace_bytes = the
+ *   workspace size when the two-kernel mode is expected to be faster (its state walk then
+ *   occupies at most half of the 256 CUs), else 0 (one kernel).  FA_ERR_INVALID_ARG for a null
+ *   pointer or a non-positive size, FA_ERR_UNSUPPORTED for DV not a multiple of 64.
  * Both validate every argument before any HIP call (FA_ERR_INVALID_ARG: null pointer, bad size,
- * Hv % Hqk, scale not finite or <= 0, unknown dtype; FA_ERR_UNSUPPORTED: DK != 128, DV not a
- * multiple of 64, misaligned pointer, strides beyond 32-bit tile offsets), return FA_ERR_LAUNCH if
+ * Hv % Hqk, scale not finite or <= 0, unknown dtype, a workspace smaller than needed;
+ * FA_ERR_UNSUPPORTED: DK != 128, DV not a multiple of 64, misaligned pointer or workspace,
+ * strides beyond 32-bit tile offsets, a grid beyond 2^31 - 1 workgroups), return FA_ERR_LAUNCH if
  * the launch fails, allocate nothing and do not synchronise.  Deterministic.
  */
 #ifndef GDN_H
 #define GDN_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -46,9 +63,11 @@ extern "C" {
 
 int gdn_kkt(const void *k, const float *g, const float *beta, void *A, int B, int T, int Hqk, int Hv, int DK,
             int dtype, void *stream);
+size_t gdn_chunk_workspace_size(int B, int T, int Hv, int DV);
+int gdn_chunk_plan(int B, int T, int Hv, int DV, size_t *workspace_bytes);
 int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *A,
                   const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv, int DK, int DV, float scale,
-                  int dtype, void *stream);
+                  int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -179,14 +179,15 @@ def test_strided_split_invalid():
 # ------------------------------------------------------------ Gated DeltaNet entry points
 
 GDN = dict(q=0x1000, k=0x2000, v=0x3000, g=0x4000, beta=0x5000, A=0x6000, s0=None, o=0x7000, sf=0x8000,
-           B=1, T=64, Hqk=1, Hv=2, DK=128, DV=128, scale=0.1, dtype=1)
+           B=1, T=64, Hqk=1, Hv=2, DK=128, DV=128, scale=0.1, dtype=1, ws=None, ws_bytes=0)
 
 
 def _gdn(**kw):
     a = dict(GDN)
     a.update(kw)
     return fa.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A"], a["s0"], a["o"], a["sf"], a["B"],
-                            a["T"], a["Hqk"], a["Hv"], a["DK"], a["DV"], a["scale"], a["dtype"], None)
+                            a["T"], a["Hqk"], a["Hv"], a["DK"], a["DV"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+                            None)
 
 
 @pytest.mark.parametrize("bad", [dict(q=None), dict(A=None), dict(sf=None), dict(T=0), dict(Hqk=2, Hv=3),
@@ -195,9 +196,34 @@ def test_gdn_invalid(bad):
     assert _gdn(**bad) == fa.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("bad", [dict(DK=64), dict(DV=96), dict(v=0x3008), dict(s0=0x9004)])
+@pytest.mark.parametrize("bad", [dict(DK=64), dict(DV=96), dict(v=0x3008), dict(s0=0x9004),
+                                 dict(ws=0x10080, ws_bytes=1 << 20)])
 def test_gdn_unsupported(bad):
     assert _gdn(**bad) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_gdn_workspace_size_and_check():
+    # chunk states (DV x 128 per chunk, 2-byte elements, end rounded up to 256 bytes), then V_new
+    # (DV x 64 per chunk)
+    for B, T, Hv, DV in [(1, 64, 2, 128), (2, 200, 4, 64), (1, 32768, 16, 128), (3, 1, 1, 64)]:
+        chunks = B * Hv * ((T + 63) // 64)
+        st = (chunks * DV * 128 * 2 + 255) // 256 * 256
+        assert fa.gdn_chunk_workspace_size(B, T, Hv, DV) == st + chunks * DV * 64 * 2
+    assert fa.gdn_chunk_workspace_size(0, 64, 2, 128) == 0
+    need = fa.gdn_chunk_workspace_size(1, 64, 2, 128)
+    assert _gdn(ws=0x100000, ws_bytes=need - 1) == fa.FA_ERR_INVALID_ARG
+
+
+def test_gdn_chunk_plan():
+    # two-kernel mode while the state walk (B * Hv * DV / 64 workgroups) fills at most 128 CUs
+    assert fa.gdn_chunk_plan(1, 32768, 16, 128) == fa.gdn_chunk_workspace_size(1, 32768, 16, 128)  # 32 walkers
+    assert fa.gdn_chunk_plan(2, 4096, 32, 128) == fa.gdn_chunk_workspace_size(2, 4096, 32, 128)    # 128
+    assert fa.gdn_chunk_plan(8, 4096, 32, 128) == 0                                                # 512
+    assert fa.gdn_chunk_plan(1, 100, 129, 64) == 0                                                 # 129
+    with pytest.raises(fa.FaError):
+        fa.gdn_chunk_plan(1, 64, 2, 96)
+    with pytest.raises(fa.FaError):
+        fa.gdn_chunk_plan(0, 64, 2, 128)
 
 
 def test_gdn_kkt_invalid():

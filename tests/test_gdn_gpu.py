@@ -71,6 +71,19 @@ def test_gdn_matches_oracle(case):
     assert _err(sf.cpu().double().numpy(), ts, "state vs token recurrence") <= 2 * TOL
 
 
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(str(x) for x in c[:5]) + str(c[5])[-4:] + str(c[6]))
+def test_gdn_two_modes_identical(case):
+    """The one-kernel mode and the state walk + parallel output kernels apply the same products
+    in the same order to the same rounded operands: their outputs and states agree bit for bit."""
+    B, T, Hqk, Hv, DV, dtype, init = case
+    w, (q, k, v, g, beta, s0) = _case(B, T, Hqk, Hv, DV, dtype, init, seed=T + Hv + 1)
+    dev = [t.cuda() if t is not None else None for t in (q, k, v, g, beta, s0)]
+    o1, s1, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, two_kernel=False)
+    o2, s2, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, two_kernel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 def test_gdn_deterministic():
     w, (q, k, v, g, beta, s0) = _case(1, 300, 2, 4, 128, torch.bfloat16, True, seed=11)
     dev = [t.cuda() for t in (q, k, v, g, beta, s0)]
@@ -92,6 +105,11 @@ def test_gdn_workload_sampled(name):
     o, sf, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale)
     torch.cuda.synchronize()
     assert torch.isfinite(sf).all() and torch.isfinite(o.float()).all()
+    for mode in (False, True):  # the library's pick equals both modes, bit for bit
+        o1, s1, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, two_kernel=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o1) and torch.equal(sf, s1), f"two_kernel={mode} differs"
+        del o1, s1
     P = 512
     sl = lambda t: t[:1, :P].contiguous() if t is not None else None  # noqa: E731
     qp, kp, vp, gp, bp = (sl(t) for t in (q, k, v, g, beta))
