@@ -421,7 +421,9 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
                     S[j] = Elem<T>::mfma(a, bv, S[j]);
                 }
         }
-        __syncthreads();  // every wave is done reading St, W', scores, V_new of this chunk
+        // No barrier before the state's operand copy is rewritten: St is read only by the first
+        // phase, which every wave finished before the first barrier of this chunk, and the work
+        // arrays written in the next chunk are read here only before the barrier that ends it.
         write_st();
 #pragma unroll
         for (int r = 0; r < 16; ++r) vcur[r] = vnext[r];
