@@ -1,10 +1,12 @@
 // fa_fwd.hip -- fused attention forward for MI355X (gfx950, CDNA4), and its C ABI.
 //
-// One workgroup computes one (batch b, query head h, query tile of BM = 128 rows); its four
-// waves own 32 query rows each.  The key/value sequence is the inner loop, in tiles of
-// BN = 64 keys ("从零开始写Qwen3", FlashAttention derivation article, section "FlashAttention"
-// and its variant note: Q tiles in parallel, KV as the inner loop).  K and V tiles are staged
-// through double-buffered LDS; Q stays in registers for the whole loop.
+// One workgroup computes one (batch b, query head h, query tile of BM = 32 W rows) with W = 8
+// waves (large grids) or 4 (small grids); each wave owns 32 query rows.  The key/value
+// sequence is the inner loop, in tiles of BN = 64 keys ("从零开始写Qwen3", FlashAttention
+// derivation article, section "FlashAttention" and its variant note: Q tiles in parallel, KV as
+// the inner loop).  K and V tiles are staged through LDS, double-buffered with 4 waves and
+// triple-buffered with 8; Q stays in registers for the whole loop.  The key-split mode (further
+// down) gives one query tile's key tiles to several workgroups and merges their results.
 //
 // Transposed formulation.  The scores are computed as S^T = K Q^T and the output as
 // O^T = V^T P^T on the 32x32x16 MFMA, so the MFMA accumulator's column index -- which is
