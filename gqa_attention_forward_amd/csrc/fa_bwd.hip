@@ -17,6 +17,9 @@
 //          registers: per 64-query tile of every query head of the group, S = Q K^T and
 //          dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (transposing reads of dO and Q).
 // No atomics: every output element has one owner, so results are deterministic.
+// Each wave raises its priority (s_setprio 1) while it issues a run of MFMAs and drops it for the
+// exp / dS arithmetic between them, so that the other wave on the SIMD fills the VALU while the
+// matrix pipe keeps taking this wave's products (3-4 % on the non-causal shapes).
 //
 // LDS tiles here are read both row-wise (16-byte MFMA operand reads, 16 lanes = 16 rows of one
 // unit) and transposed (8-byte transposing reads, 32 lanes = 4 rows x 4 units), so instead of
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -225,6 +229,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
                 dp[kb] = Elem<T>::mfma(read_row<D>(vt, kb * 32 + ql, 2 * ks + hh), dreg[ks], dp[kb]);
             }
         // dS^T = P^T (dP^T - Delta); register r of block kb is key n0 + 32 kb + 8 (r/4) + 4 hh + r%4
+        __builtin_amdgcn_s_setprio(0);
         const int n0 = t * kTile;
         const bool masked = t >= kr.n_full;
 #pragma unroll
@@ -237,6 +242,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
                 s[kb][r] = pr * (dp[kb][r] - delta);
             }
         // dQ^T += K^T dS^T
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -246,6 +252,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
                 for (int db = 0; db < DB; ++db)
                     acc[db] = Elem<T>::mfma(read_tr<D>(kt, tro, kb * 32 + 16 * tt, db), b, acc[db]);
             }
+        __builtin_amdgcn_s_setprio(0);
     }
     if (qvalid) {
         T *dst = (T *)p.dq + (bh * M + qrow) * D + hh * 16;
@@ -338,11 +345,13 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
             f32x16 s, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s = Elem<T>::mfma(read_row<D>(qtile, qb * 32 + kl, 2 * ks + hh), kreg[ks], s);
                 dp = Elem<T>::mfma(read_row<D>(dtile, qb * 32 + kl, 2 * ks + hh), vreg[ks], dp);
             }
+            __builtin_amdgcn_s_setprio(0);
             // register r is query i0 + 32 qb + 8 (r/4) + 4 hh + r%4 of this lane's key; P replaces
             // S and dS replaces dP in place
 #pragma unroll
@@ -363,6 +372,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
                 }
             }
             // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const u32x4 bp = pack_b<T>(s, tt), bs = pack_b<T>(dp, tt);
@@ -372,6 +382,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
                     dk[db] = Elem<T>::mfma(read_tr<D>(qtile, tro, qb * 32 + 16 * tt, db), bs, dk[db]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     }
     if (kvalid) {
