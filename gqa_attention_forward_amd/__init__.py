@@ -241,10 +241,10 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
 
     split_kv: "auto" runs the key-split forward when its plan splits some query tile (small
     grids) or when M < 128 with grouped KV heads (the key-split kernel then stacks the query
-    heads of a group into one tile's rows), and fa_fwd otherwise; False always runs fa_fwd; an int > 0 runs the key-split forward
-    with at most that many key tiles per share.  The split workspace comes from torch's caching
-    allocator.  Kernels are enqueued on `stream` (default: torch's current stream) and not
-    waited for."""
+    heads of a group into one tile's rows), and fa_fwd otherwise; False always runs fa_fwd;
+    an int > 0 runs the key-split forward with at most that many key tiles per share.  The
+    split workspace comes from torch's caching allocator.  Kernels are enqueued on `stream`
+    (default: torch's current stream) and not waited for."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
