@@ -374,5 +374,8 @@ def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, s
     return o, sf, A
 
 
-__all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_chunk_plan", "gdn_prefill", "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided", "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides", "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+__all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_chunk_plan", "gdn_prefill",
+           "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided",
+           "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides",
+           "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]
