@@ -229,3 +229,20 @@ def test_gdn_chunk_plan():
 def test_gdn_kkt_invalid():
     assert fa.gdn_kkt(None, 0x4000, 0x5000, 0x6000, 1, 64, 1, 2, 128, 1, None) == fa.FA_ERR_INVALID_ARG
     assert fa.gdn_kkt(0x2000, 0x4000, 0x5000, 0x6000, 1, 64, 1, 2, 64, 1, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_headers_are_plain_c(tmp_path):
+    # include/*.h must compile as strict C99 and as C++ (no C++ or HIP types in the ABI)
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "use.c"
+    src.write_text("".join(f'#include "{h}"\n' for h in sorted(os.listdir(inc)) if h.endswith(".h")) +
+                   "int main(void) { return 0; }\n")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-I", inc, str(src)],
+                   check=True)
+    subprocess.run(["g++", "-std=c++11", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c++", "-I", inc,
+                    str(src)], check=True)
