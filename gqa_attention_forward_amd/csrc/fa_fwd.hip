@@ -1,12 +1,15 @@
 // fa_fwd.hip -- fused attention forward for MI355X (gfx950, CDNA4), and its C ABI.
 //
-// One workgroup computes one (batch b, query head h, query tile of BM = 32 W rows) with W = 8
-// waves (large grids) or 4 (small grids); each wave owns 32 query rows.  The key/value
-// sequence is the inner loop, in tiles of BN = 64 keys ("从零开始写Qwen3", FlashAttention
-// derivation article, section "FlashAttention" and its variant note: Q tiles in parallel, KV as
-// the inner loop).  K and V tiles are staged through LDS, double-buffered with 4 waves and
-// triple-buffered with 8; Q stays in registers for the whole loop.  The key-split mode (further
-// down) gives one query tile's key tiles to several workgroups and merges their results.
+// One workgroup computes one (batch b, query head h, query tile of BM rows): 8 waves over 256
+// rows on large grids, 4 waves over 128 rows on small ones, or -- small grids with long key
+// ranges -- 8 waves over 128 rows in two key groups of 4 that share the key tiles out
+// between them and merge their softmax states at the end.  Each wave of a group owns 32
+// query rows.  The key/value sequence is the inner loop, in tiles of BN = 64 keys
+// ("从零开始写Qwen3", FlashAttention derivation article, section "FlashAttention" and its
+// variant note: Q tiles in parallel, KV as the inner loop).  K and V tiles are staged through
+// LDS, double-buffered per 4-wave group and triple-buffered with 8 waves on 256 rows; Q stays
+// in registers for the whole loop.  The key-split mode (further down) gives one query tile's
+// key tiles to several workgroups and merges their results.
 //
 // Transposed formulation.  The scores are computed as S^T = K Q^T and the output as
 // O^T = V^T P^T on the 32x32x16 MFMA, so the MFMA accumulator's column index -- which is
@@ -110,14 +113,24 @@ struct SplitParams : Params {
 
 // --------------------------------------------------------------------- kernel
 
-// W waves per workgroup (BM = 32 W query rows).  W = 4: two workgroups share a CU, K and V
-// tiles double-buffered.  W = 8: one workgroup per CU (still two waves per SIMD), tiles
+// W waves per workgroup (KG = 1: BM = 32 W query rows).  W = 4: two workgroups share a CU, K
+// and V tiles double-buffered.  W = 8: one workgroup per CU (still two waves per SIMD), tiles
 // triple-buffered so that each load has two tiles of time to land.
-template <typename T, int D, bool CAUSAL, int W, bool SPLIT, typename P>
+//
+// KG = 2 (small grids): the W waves form two key groups of W / 2 waves over the same BM =
+// 16 W rows; group k takes the query tile's key tiles k, k + 2, ... with buffers of its own,
+// both groups walk the same number of tiles (the second one's last tile, when the count is
+// odd, lies past the visible range and is masked out entirely), and the second group's
+// running max, partial sums and output accumulators are merged into the first group's
+// through LDS before the epilogue: half the sequential key loop per workgroup, and two waves
+// per SIMD instead of one.
+template <typename T, int D, bool CAUSAL, int W, bool SPLIT, int KG, typename P>
 __device__ __forceinline__ void fa_fwd_body(const P &p)
 {
-    constexpr int kBM = 32 * W, kWaves = W;
-    constexpr int NBUF = W == 8 ? 3 : 2;
+    static_assert(KG == 1 || (KG == 2 && !SPLIT), "key groups only in the plain kernel");
+    constexpr int WG = W / KG;  // waves of one key group
+    constexpr int kBM = 32 * WG, kWaves = WG;
+    constexpr int NBUF = KG == 1 && W == 8 ? 3 : 2;
     constexpr int UNITS = D / 8;                       // 16-byte units per row
     constexpr int KS = D / 16;                         // MFMA k-steps over the head dimension
     constexpr int KB = kBN / 32;                       // 32-key blocks per tile
@@ -126,13 +139,16 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     constexpr bool SWZ = Lds<D>::SWZ;
     constexpr int K_TILE = kBN * KP, V_TILE = kBN * VP;
 
-    // [K buf 0 .. NBUF-1 | V buf 0 .. NBUF-1 | 1 KiB sink for padding loads]
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[NBUF * (K_TILE + V_TILE) + 1024];
+    // per key group [K buf 0 .. NBUF-1 | V buf 0 .. NBUF-1], then a 1 KiB sink for padding loads
+    constexpr int GROUP_BYTES = NBUF * (K_TILE + V_TILE);
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[KG * GROUP_BYTES + 1024];
     lds_u8 *smem = (lds_u8 *)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane((tid >> 6) / WG);  // key group
+    const int wave = (tid >> 6) % WG;  // wave inside the key group
+    lds_u8 *const gsmem = smem + grp * GROUP_BYTES;  // this group's tile buffers
     const int ql = lane & 31;   // query column of this lane inside the wave's 32 rows
     const int hh = lane >> 5;   // which half of each 32-key block this lane holds
 
@@ -171,9 +187,11 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     const int m0 = tc.qt * kBM;
     const int M = p.M, N = p.N;
     const KvRange kr = SPLIT ? unit_kv_range(m0, kBM, kBN, M, N, R, CAUSAL) : kv_range(m0, kBM, kBN, M, N, CAUSAL);
-    // key tiles [t0, t0 + n_tiles) of the query tile's visible range are this workgroup's
+    // key tiles [t0, t0 + n_tiles) of the query tile's visible range are this workgroup's; its
+    // key group grp walks n_loc of them: t0 + KG i + grp for i < n_loc
     const int t0 = split * kr.n_tiles / n_split;
     const int n_tiles = (split + 1) * kr.n_tiles / n_split - t0;
+    const int n_loc = (n_tiles + KG - 1) / KG;
 
     const T *kg = (const T *)p.k + tc.b * p.k_sb + hk * p.k_sh;
     const T *vg = (const T *)p.v + tc.b * p.v_sb + hk * p.v_sh;
@@ -209,7 +227,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     constexpr int LOADS_PER_TILE = KI + VI;  // per wave
     static_assert(LOADS_PER_TILE < 16, "wait count encoding");
     constexpr unsigned kPad = 0x7fffff00u;  // an offset past the end of every tile resource
-    lds_u8 *const sink = smem + NBUF * (K_TILE + V_TILE);
+    lds_u8 *const sink = smem + KG * GROUP_BYTES;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // key rows at or past kv_end read as zero: the end of the keys, or of this workgroup's share
     // (the pipeline's look-ahead loads run past it)
@@ -238,9 +256,9 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + (long long)r0 * row_bytes), (short)0,
                                                  bytes, 0x00020000);
     };
-    auto load_k = [&](int t, int buf) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, k_rs, t0 + t);
-        lds_u8 *dst = smem + buf * K_TILE;
+    auto load_k = [&](int t, int buf) {  // the group's tile t
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, k_rs, t0 + KG * t + grp);
+        lds_u8 *dst = gsmem + buf * K_TILE;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
             const int j = wave_u + kWaves * i;
@@ -248,8 +266,8 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         }
     };
     auto load_v = [&](int t, int buf) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, v_rs, t0 + t);
-        lds_u8 *dst = smem + NBUF * K_TILE + buf * V_TILE;
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, v_rs, t0 + KG * t + grp);
+        lds_u8 *dst = gsmem + NBUF * K_TILE + buf * V_TILE;
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
             const int j = wave_u + kWaves * i;
@@ -299,7 +317,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
 
     // mask (unless `none`) the scores of tile t, then return their in-lane max
     auto mask_max = [&](int t, f32x16 (&sc)[KB], bool none = false) {
-        const int n0 = (t0 + t) * kBN;
+        const int n0 = (t0 + KG * t + grp) * kBN;
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -380,8 +398,8 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         constexpr bool QK = decltype(qk_tag)::value;
         float mc = 0.f;  // m * c of tile t, set by the running-max update inside the sequence
         constexpr int J0 = QK ? 0 : NM;  // first MFMA of the sequence
-        const lds_u8 *kp = smem + kbuf * K_TILE + k_rd;
-        const lds_u8 *vp = smem + NBUF * K_TILE + vbuf * V_TILE + v_rd;
+        const lds_u8 *kp = gsmem + kbuf * K_TILE + k_rd;
+        const lds_u8 *vp = gsmem + NBUF * K_TILE + vbuf * V_TILE + v_rd;
         if constexpr (QK) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -456,7 +474,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
 
     // scores of one tile only (the first one)
     auto scores = [&](int kbuf, f32x16 (&s)[KB]) {
-        const lds_u8 *kp = smem + kbuf * K_TILE + k_rd;
+        const lds_u8 *kp = gsmem + kbuf * K_TILE + k_rd;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -472,7 +490,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     // NBUF-2 iterations earlier.
     f32x16 s_cur[KB], s_nxt[KB];
     float mt_pending = -INFINITY;  // in-lane max of the scores whose running-max update is pending
-    if (n_tiles > 0) {
+    if (n_loc > 0) {
         load_k(0, 0);
         load_v(0, 0);
         load_k(1, 1);
@@ -485,7 +503,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         }
         __syncthreads();
         scores(0, s_cur);
-        mt_pending = mask_max(0, s_cur, t0 < kr.n_full);
+        mt_pending = mask_max(0, s_cur, t0 + grp < kr.n_full);
         __syncthreads();  // every wave has read K_0 before its buffer is refilled
     }
     int kb_next = 1 % NBUF, vb_cur = 0, b_load = 0;  // buffers of K_{t+1}, V_t, and of the loads (t % NBUF)
@@ -497,7 +515,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         float psum = 0.f;
         float mt = step(std::true_type{}, kb_next, vb_cur, nxt, cur, mt_pending, psum);
         l_part += psum;
-        if (t0 + t + 1 >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
+        if (t0 + KG * (t + 1) + grp >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
         mt_pending = mt;
         if constexpr (NBUF == 3)
             wait_loads(Keep1{});
@@ -510,7 +528,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     };
     // Full steps come in pairs with the two score arrays swapping roles (no copies); an odd
     // count starts with one step and one copy.
-    const int n_steps = n_tiles - 1;
+    const int n_steps = n_loc - 1;
     int t = 0;
     if (n_steps > 0 && (n_steps & 1)) {
         body(0, s_cur, s_nxt);
@@ -522,12 +540,44 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         body(t, s_cur, s_nxt);
         body(t + 1, s_nxt, s_cur);
     }
-    if (n_tiles > 0) {  // last tile: no scores to prefetch
+    if (n_loc > 0) {  // last tile: no scores to prefetch
         const float mc = update_max(mt_pending);
         probs(s_cur, mc);
         float psum = 0.f;
         step(std::false_type{}, 0, vb_cur, s_nxt, s_cur, -INFINITY, psum);
         l_part += psum;
+    }
+
+    if constexpr (KG == 2) {
+        // merge the second key group's state into the first's, lane by lane (both hold the same
+        // rows in the same layout): value v of lane (wave, lane) at float (v * 64 WG + 64 wave + lane)
+        __attribute__((address_space(3))) float *xf = (__attribute__((address_space(3))) float *)smem;
+        constexpr int NV = DB * 16;
+        static_assert((NV + 2) * 64 * WG * 4 <= KG * GROUP_BYTES, "merge area inside the tile buffers");
+        const int slot = wave * 64 + lane;
+        wait_loads(Keep0{});  // no load into LDS still in flight (the look-ahead ones included)
+        __syncthreads();      // and every wave is done with the tile buffers
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xf[(db * 16 + r) * 64 * WG + slot] = oacc[db][r];
+            xf[NV * 64 * WG + slot] = m_run;
+            xf[(NV + 1) * 64 * WG + slot] = l_part;
+        }
+        __syncthreads();
+        if (grp == 0) {
+            const float m1 = xf[NV * 64 * WG + slot], l1 = xf[(NV + 1) * 64 * WG + slot];
+            const float m = fmaxf(m_run, m1);
+            const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * c);
+            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c);
+            l_part = a0 * l_part + a1 * l1;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] = a0 * oacc[db][r] + a1 * xf[(db * 16 + r) * 64 * WG + slot];
+            m_run = m;
+        }
     }
 
     // ---- A8: epilogue -- normalise once, write O and the logsumexp
@@ -537,7 +587,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
                                                    __builtin_bit_cast(unsigned, l_part), false, false);
         l_tot = __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
     }
-    if (qvalid) {
+    if (qvalid && grp == 0) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse = l_tot > 0.f ? (m_run * c + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
         const size_t row = ((size_t)tc.b * p.Hq + qhead) * (size_t)M + qpos;
@@ -576,17 +626,17 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     }
 }
 
-template <typename T, int D, bool CAUSAL, int W>
+template <typename T, int D, bool CAUSAL, int W, int KG>
 __global__ __launch_bounds__(64 * W, 2) void fa_fwd_kernel(Params p)
 {
-    fa_fwd_body<T, D, CAUSAL, W, false>(p);
+    fa_fwd_body<T, D, CAUSAL, W, false, KG>(p);
 }
 
 // one share of a query tile's keys (key-split mode)
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fa_fwd_split_kernel(SplitParams p)
 {
-    fa_fwd_body<T, D, CAUSAL, 4, true>(p);
+    fa_fwd_body<T, D, CAUSAL, 4, true, 1>(p);
 }
 
 // Merge of the key shares of the split query tiles: with share lse_s (natural log) and
@@ -633,38 +683,62 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(SplitParams p)
 
 // ------------------------------------------------------------------ host side
 
-// Launch plan: 8-wave workgroups (256 query rows) when they alone fill every CU once,
-// 4-wave workgroups otherwise (small grids need the larger workgroup count).
-static int waves_for(int B, int Hq, int M)
+// Launch plan: 8-wave workgroups over 256 query rows when they alone fill every CU once,
+// 128-row query tiles otherwise (small grids need the larger workgroup count).  A 128-row
+// grid that leaves CUs with one workgroup at most runs 8-wave workgroups with two key groups
+// when the longest key range has kMinKgTiles tiles or more: with a single 4-wave workgroup
+// on a CU each SIMD runs one wave, and the second group's wave adds throughput (measured
+// about 8 % per key tile with every CU busy, 17 % with 32 workgroups), while the merge and
+// the larger workgroup add a fixed cost (about 2 us) that short key ranges do not win back.
+constexpr int kNumCUs = 256;      // compute units of an MI355X
+constexpr int kMinKgTiles = 16;   // key tiles of the longest range for two key groups
+struct LaunchShape {
+    int W;   // waves per workgroup
+    int KG;  // key groups
+};
+static bool tiles_256(int B, int Hq, int M)
 {
-    const long long wg8 = (long long)B * Hq * ((M + 255) / 256);
-    return wg8 >= 256 ? 8 : 4;
+    return (long long)B * Hq * ((M + 255) / 256) >= kNumCUs;
+}
+static LaunchShape launch_shape(int B, int Hq, int M, int N)
+{
+    if (tiles_256(B, Hq, M)) return {8, 1};
+    const long long wg128 = (long long)B * Hq * ((M + 127) / 128);
+    // the longest key range of any query tile is the whole key sequence (the last tile's, when causal)
+    if (wg128 <= kNumCUs && (N + kBN - 1) / kBN >= kMinKgTiles) return {8, 2};
+    return {4, 1};
 }
 
 static int tile_shape(int B, int Hq, int M, int D, int *BM, int *BN)
 {
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-    *BM = 32 * waves_for(B, Hq, M);
+    *BM = tiles_256(B, Hq, M) ? 256 : 128;
     *BN = kBN;
     return FA_OK;
 }
 
-template <typename T, int D, int W>
+template <typename T, int D, int W, int KG>
 static hipError_t launch_w(const Params &p, bool causal, hipStream_t stream)
 {
     dim3 grid((unsigned)p.total), block(64 * W);
     if (causal)
-        hipLaunchKernelGGL((fa_fwd_kernel<T, D, true, W>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, true, W, KG>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, W>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, W, KG>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_t(const Params &p, int D, int W, bool causal, hipStream_t stream)
+template <typename T, int D>
+static hipError_t launch_d(const Params &p, LaunchShape ls, bool causal, hipStream_t stream)
 {
-    if (D == 128) return W == 8 ? launch_w<T, 128, 8>(p, causal, stream) : launch_w<T, 128, 4>(p, causal, stream);
-    return W == 8 ? launch_w<T, 64, 8>(p, causal, stream) : launch_w<T, 64, 4>(p, causal, stream);
+    if (ls.KG == 2) return launch_w<T, D, 8, 2>(p, causal, stream);
+    return ls.W == 8 ? launch_w<T, D, 8, 1>(p, causal, stream) : launch_w<T, D, 4, 1>(p, causal, stream);
+}
+
+template <typename T>
+static hipError_t launch_t(const Params &p, int D, LaunchShape ls, bool causal, hipStream_t stream)
+{
+    return D == 128 ? launch_d<T, 128>(p, ls, causal, stream) : launch_d<T, 64>(p, ls, causal, stream);
 }
 
 // ---- key-split mode (4-wave workgroups, 128-row query tiles)
@@ -890,9 +964,9 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
     if (p.total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;  // one-dimensional grid limit
 
     hipStream_t s = (hipStream_t)stream;
-    const int W = BM / 32;
-    hipError_t err = dtype == FA_F16 ? fa::launch_t<_Float16>(p, D, W, causal != 0, s)
-                                     : fa::launch_t<__bf16>(p, D, W, causal != 0, s);
+    const fa::LaunchShape ls = fa::launch_shape(B, Hq, M, N);
+    hipError_t err = dtype == FA_F16 ? fa::launch_t<_Float16>(p, D, ls, causal != 0, s)
+                                     : fa::launch_t<__bf16>(p, D, ls, causal != 0, s);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

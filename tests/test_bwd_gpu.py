@@ -69,7 +69,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(str(x) for x in s[:7]) + str(s[7])[-4:])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(str(x) for x in s[:7]) + str(s[7]).split(".")[-1])
 def test_bwd_matches_oracle(shape):
     got, ref = _run(shape, seed=sum(shape[:6]))
     _check(got, ref, shape[7], f"bwd {shape}")

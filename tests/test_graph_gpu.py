@@ -49,9 +49,16 @@ def _capture_and_replay(fn, what):
         assert all(torch.equal(x, y) for x, y in zip(eager, ref)), what
 
 
-@pytest.mark.parametrize("split_kv", [False, "auto"])
-def test_forward_capture(split_kv):
-    B, Hq, Hkv, M, N, D = (1, 8, 2, 300, 700, 128) if split_kv is False else (4, 16, 4, 1, 4096, 128)
+FWD_CASES = {  # split_kv, shape (B, Hq, Hkv, M, N, D)
+    "plain": (False, (1, 8, 2, 300, 700, 128)),
+    "plain_key_groups": (False, (1, 8, 2, 300, 1100, 128)),  # 17 key tiles on a small grid
+    "split": ("auto", (4, 16, 4, 1, 4096, 128)),
+}
+
+
+@pytest.mark.parametrize("case", list(FWD_CASES))
+def test_forward_capture(case):
+    split_kv, (B, Hq, Hkv, M, N, D) = FWD_CASES[case]
     q, k, v = (t.cuda() for t in make_custom(B, Hq, Hkv, M, N, D, torch.bfloat16, seed=71))
     scale = 1 / math.sqrt(D)
 

@@ -64,10 +64,19 @@ SMALL = [
     (1, 2, 2, 100, 333, 64, False, torch.float16),
     (1, 2, 1, 64, 130, 128, False, torch.bfloat16),
     (1, 3, 1, 400, 100, 128, True, torch.float16),       # M > N: whole query tiles with no key
+    # small grids with 16+ key tiles: 8-wave workgroups whose two key groups split the tiles,
+    # with even and odd tile counts, ragged N, masked rows (M > N) and a single query row
+    (1, 2, 1, 128, 1024, 128, True, torch.float16),
+    (1, 4, 2, 300, 1023, 128, True, torch.bfloat16),
+    (2, 2, 2, 200, 1030, 64, False, torch.float16),      # 17 tiles: the second group pads one
+    (1, 2, 1, 1200, 1000, 128, True, torch.bfloat16),    # first 200 rows see no key
+    (1, 4, 1, 77, 2049, 128, True, torch.float16),
+    (1, 8, 8, 1, 1500, 64, True, torch.bfloat16),
+    (3, 5, 5, 129, 1300, 128, False, torch.float16),
 ]
 
 
-@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(str(x) for x in s[:7]) + str(s[7])[-4:])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(str(x) for x in s[:7]) + str(s[7]).split(".")[-1])
 def test_small_shapes_full_compare(shape):
     B, Hq, Hkv, M, N, D, causal, dtype = shape
     q, k, v = make_custom(B, Hq, Hkv, M, N, D, dtype, seed=M * 7 + N)

@@ -5,7 +5,8 @@ Forward: batch 1-3, 1-4 KV heads with 1, 2, 4 or 8 query heads each, M and N fro
 values (1, 63-65, 127-129, 255-257) and uniform draws up to 700/900, both head dims, both
 masks, both input types, optionally 1 % of K rows scaled by 8, through every path: the plain
 kernel, the key-split kernel with the automatic plan and with forced shares of 1 and 4 key
-tiles, and strided [B, S, H, D] buffers.  Backward and the Gated DeltaNet prefill get smaller
+tiles, and strided [B, S, H, D] buffers; 12 more draws with 961-2600 keys on small grids
+take the plain kernel's two-key-group workgroups.  Backward and the Gated DeltaNet prefill get smaller
 sweeps of the same kind.  The draws are fixed (seeded), so a failure names a reproducible case.
 """
 import math
@@ -48,12 +49,32 @@ def _fwd_cases(n, seed):
     return cases
 
 
+def _kg_cases(n, seed):
+    """Small grids (at most 256 query tiles of 128 rows) with 961 keys or more: the plain
+    kernel then splits each query tile's key tiles between two key groups."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        Hkv = int(rng.integers(1, 4))
+        g = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        M, N = _size(rng, 500), int(rng.integers(961, 2600))
+        D = int(rng.choice([64, 128]))
+        if B * Hkv * g * M * N * D > 3e9:
+            continue
+        causal = bool(rng.random() < 0.6)
+        dtype = torch.float16 if rng.random() < 0.5 else torch.bfloat16
+        peak = 0.01 if rng.random() < 0.3 else 0.0
+        cases.append((B, Hkv * g, Hkv, M, N, D, causal, dtype, "plain", peak, 100 + len(cases)))
+    return cases
+
+
 def _id(c):
     B, Hq, Hkv, M, N, D, causal, dtype, mode, peak, i = c
-    return f"{i}-{B}x{Hq}x{Hkv}x{M}x{N}x{D}-{'c' if causal else 'n'}-{str(dtype)[-4:]}-{mode}{'-peaky' if peak else ''}"
+    return f"{i}-{B}x{Hq}x{Hkv}x{M}x{N}x{D}-{'c' if causal else 'n'}-{str(dtype).split('.')[-1]}-{mode}{'-peaky' if peak else ''}"
 
 
-@pytest.mark.parametrize("case", _fwd_cases(48, 20251), ids=_id)
+@pytest.mark.parametrize("case", _fwd_cases(48, 20251) + _kg_cases(12, 20254), ids=_id)
 def test_forward_random(case):
     B, Hq, Hkv, M, N, D, causal, dtype, mode, peak, i = case
     q, k, v = make_custom(B, Hq, Hkv, M, N, D, dtype, seed=1000 + i, peak_rate=peak)
@@ -93,7 +114,7 @@ def _bwd_cases(n, seed):
 
 
 @pytest.mark.parametrize("case", _bwd_cases(16, 20252),
-                         ids=lambda c: f"{c[8]}-{'x'.join(str(x) for x in c[:6])}-{'c' if c[6] else 'n'}-{str(c[7])[-4:]}")
+                         ids=lambda c: f"{c[8]}-{'x'.join(str(x) for x in c[:6])}-{'c' if c[6] else 'n'}-{str(c[7]).split('.')[-1]}")
 def test_backward_random(case):
     B, Hq, Hkv, M, N, D, causal, dtype, i = case
     q, k, v = make_custom(B, Hq, Hkv, M, N, D, dtype, seed=2000 + i)
@@ -133,7 +154,7 @@ def _gdn_cases(n, seed):
 
 
 @pytest.mark.parametrize("case", _gdn_cases(10, 20253),
-                         ids=lambda c: f"{c[8]}-{'x'.join(str(x) for x in c[:5])}-{str(c[5])[-4:]}-s0{int(c[6])}-two{int(c[7])}")
+                         ids=lambda c: f"{c[8]}-{'x'.join(str(x) for x in c[:5])}-{str(c[5]).split('.')[-1]}-s0{int(c[6])}-two{int(c[7])}")
 def test_gdn_random(case):
     B, T, Hqk, Hv, DV, dtype, init, two, i = case
     w = GdnWorkload("rand", B, T, Hqk, Hv, 128, DV, dtype, 4000 + i, init_state=init)

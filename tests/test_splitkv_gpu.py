@@ -63,7 +63,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(str(x) for x in s[:7]) + str(s[7])[-4:] + f"t{s[8]}")
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(str(x) for x in s[:7]) + str(s[7]).split(".")[-1] + f"t{s[8]}")
 def test_splitkv_small_shapes(shape):
     B, Hq, Hkv, M, N, D, causal, dtype, tiles = shape
     q, k, v = make_custom(B, Hq, Hkv, M, N, D, dtype, seed=M * 13 + N)
