@@ -19,7 +19,9 @@
 // No atomics: every output element has one owner, so results are deterministic.
 // Each wave raises its priority (s_setprio 1) while it issues a run of MFMAs and drops it for the
 // exp / dS arithmetic between them, so that the other wave on the SIMD fills the VALU while the
-// matrix pipe keeps taking this wave's products (3-4 % on the non-causal shapes).
+// matrix pipe keeps taking this wave's products (3-4 % on the non-causal shapes).  Inside a run,
+// the LDS operand of each MFMA is read a few MFMAs ahead (mfma_run) rather than just before it,
+// so the LDS latency does not stall every product.
 //
 // LDS tiles here are read both row-wise (16-byte MFMA operand reads, 16 lanes = 16 rows of one
 // unit) and transposed (8-byte transposing reads, 32 lanes = 4 rows x 4 units), so instead of
@@ -30,6 +32,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "fa.h"
 #include "fa_device.h"
 #include "fa_swizzle.h"
@@ -37,6 +42,34 @@
 
 namespace fa {
 namespace bwd {
+
+// f(integral_constant<int, j>) for j = B .. E-1, expanded at compile time (every index a constant)
+template <int B, typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, J...>)
+{
+    (f(std::integral_constant<int, B + J>{}), ...);
+}
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
+}
+
+// Runs N MFMAs, MFMA m taking its LDS operand read(m): the read of MFMA m + RA is issued
+// before MFMA m (RA reads in flight), and scheduling barriers keep that order, so the LDS
+// latency hides behind the MFMAs instead of stalling each one.
+template <int N, int RA, typename Read, typename Mfma>
+__device__ __forceinline__ void mfma_run(Read &&read, Mfma &&mfma)
+{
+    u32x4 a[RA + 1];
+    static_for<0, RA>([&](auto mc) { a[decltype(mc)::value] = read(mc); });
+    static_for<0, N>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m + RA < N) a[(m + RA) % (RA + 1)] = read(std::integral_constant<int, m + RA>{});
+        mfma(mc, a[m % (RA + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+constexpr int kReadAhead = 3;  // LDS operand reads in flight ahead of the MFMA that uses them
 
 constexpr int kRows = 128;  // rows a workgroup owns (4 waves x 32)
 constexpr int kTile = 64;   // rows of the inner-loop tile
@@ -221,13 +254,19 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
         __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = Elem<T>::mfma(read_row<D>(kt, kb * 32 + ql, 2 * ks + hh), qreg[ks], s[kb]);
-                dp[kb] = Elem<T>::mfma(read_row<D>(vt, kb * 32 + ql, 2 * ks + hh), dreg[ks], dp[kb]);
-            }
+        // MFMA m: k-step m / 4 of key block (m / 2) % 2, of S (m even, K rows) or dP (m odd, V rows)
+        mfma_run<4 * KS, kReadAhead>(
+            [&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                return read_row<D>(m % 2 ? vt : kt, ((m / 2) % 2) * 32 + ql, 2 * (m / 4) + hh);
+            },
+            [&](auto mc, const u32x4 &a) {
+                constexpr int m = decltype(mc)::value, kb = (m / 2) % 2;
+                if constexpr (m % 2 == 0)
+                    s[kb] = Elem<T>::mfma(a, qreg[m / 4], s[kb]);
+                else
+                    dp[kb] = Elem<T>::mfma(a, dreg[m / 4], dp[kb]);
+            });
         // dS^T = P^T (dP^T - Delta); register r of block kb is key n0 + 32 kb + 8 (r/4) + 4 hh + r%4
         __builtin_amdgcn_s_setprio(0);
         const int n0 = t * kTile;
@@ -373,13 +412,38 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
             }
             // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries
             __builtin_amdgcn_s_setprio(1);
+            if constexpr (CAUSAL) {
+                // transposing reads issued kReadAhead MFMAs ahead (1-6 % faster on the causal
+                // shapes; the non-causal kernel spilled inside the loop with it and ran 2-4 %
+                // slower, so it keeps the plain loop below).
+                // MFMA m: k-step tt = m / (2 DB) of column block db = (m / 2) % DB, of dV (m even,
+                // dO^T by P) or of dK (m odd, Q^T by dS)
+                u32x4 bp = pack_b<T>(s, 0), bs = pack_b<T>(dp, 0);
+                mfma_run<4 * DB, kReadAhead>(
+                    [&](auto mc) {
+                        constexpr int m = decltype(mc)::value;
+                        return read_tr<D>(m % 2 ? qtile : dtile, tro, qb * 32 + 16 * (m / (2 * DB)), (m / 2) % DB);
+                    },
+                    [&](auto mc, const u32x4 &a) {
+                        constexpr int m = decltype(mc)::value, db = (m / 2) % DB;
+                        if constexpr (m == 2 * DB) {
+                            bp = pack_b<T>(s, 1);
+                            bs = pack_b<T>(dp, 1);
+                        }
+                        if constexpr (m % 2 == 0)
+                            dv[db] = Elem<T>::mfma(a, bp, dv[db]);
+                        else
+                            dk[db] = Elem<T>::mfma(a, bs, dk[db]);
+                    });
+            } else {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const u32x4 bp = pack_b<T>(s, tt), bs = pack_b<T>(dp, tt);
+                for (int tt = 0; tt < 2; ++tt) {
+                    const u32x4 bp = pack_b<T>(s, tt), bs = pack_b<T>(dp, tt);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dv[db] = Elem<T>::mfma(read_tr<D>(dtile, tro, qb * 32 + 16 * tt, db), bp, dv[db]);
-                    dk[db] = Elem<T>::mfma(read_tr<D>(qtile, tro, qb * 32 + 16 * tt, db), bs, dk[db]);
+                    for (int db = 0; db < DB; ++db) {
+                        dv[db] = Elem<T>::mfma(read_tr<D>(dtile, tro, qb * 32 + 16 * tt, db), bp, dv[db]);
+                        dk[db] = Elem<T>::mfma(read_tr<D>(qtile, tro, qb * 32 + 16 * tt, db), bs, dk[db]);
+                    }
                 }
             }
             __builtin_amdgcn_s_setprio(0);
