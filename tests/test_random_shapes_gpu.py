@@ -6,7 +6,7 @@ values (1, 63-65, 127-129, 255-257) and uniform draws up to 700/900, both head d
 masks, both input types, optionally 1 % of K rows scaled by 8, through every path: the plain
 kernel, the key-split kernel with the automatic plan and with forced shares of 1 and 4 key
 tiles, and strided [B, S, H, D] buffers; 12 more draws with 961-2600 keys on small grids
-take the plain kernel's two-key-group workgroups.  Backward and the Gated DeltaNet prefill get smaller
+(contiguous or [B, S, H, D]) take the plain kernel's two-key-group workgroups.  Backward and the Gated DeltaNet prefill get smaller
 sweeps of the same kind.  The draws are fixed (seeded), so a failure names a reproducible case.
 """
 import math
@@ -65,7 +65,8 @@ def _kg_cases(n, seed):
         causal = bool(rng.random() < 0.6)
         dtype = torch.float16 if rng.random() < 0.5 else torch.bfloat16
         peak = 0.01 if rng.random() < 0.3 else 0.0
-        cases.append((B, Hkv * g, Hkv, M, N, D, causal, dtype, "plain", peak, 100 + len(cases)))
+        mode = "bshd" if rng.random() < 0.3 else "plain"
+        cases.append((B, Hkv * g, Hkv, M, N, D, causal, dtype, mode, peak, 100 + len(cases)))
     return cases
 
 
