@@ -32,44 +32,16 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <type_traits>
-#include <utility>
-
 #include "fa.h"
 #include "fa_device.h"
+#include "fa_mfma_run.h"
 #include "fa_swizzle.h"
 #include "fa_tiles.h"
 
 namespace fa {
 namespace bwd {
 
-// f(integral_constant<int, j>) for j = B .. E-1, expanded at compile time (every index a constant)
-template <int B, typename F, int... J>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, J...>)
-{
-    (f(std::integral_constant<int, B + J>{}), ...);
-}
-template <int B, int E, typename F> __device__ __forceinline__ void static_for(F &&f)
-{
-    static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
-}
-
-// Runs N MFMAs, MFMA m taking its LDS operand read(m): the read of MFMA m + RA is issued
-// before MFMA m (RA reads in flight), and scheduling barriers keep that order, so the LDS
-// latency hides behind the MFMAs instead of stalling each one.
-template <int N, int RA, typename Read, typename Mfma>
-__device__ __forceinline__ void mfma_run(Read &&read, Mfma &&mfma)
-{
-    u32x4 a[RA + 1];
-    static_for<0, RA>([&](auto mc) { a[decltype(mc)::value] = read(mc); });
-    static_for<0, N>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        if constexpr (m + RA < N) a[(m + RA) % (RA + 1)] = read(std::integral_constant<int, m + RA>{});
-        mfma(mc, a[m % (RA + 1)]);
-        __builtin_amdgcn_sched_barrier(0);
-    });
-}
-constexpr int kReadAhead = 3;  // LDS operand reads in flight ahead of the MFMA that uses them
+constexpr int kReadAhead = 3;  // LDS operand reads in flight ahead of the MFMA that uses them (mfma_run)
 
 constexpr int kRows = 128;  // rows a workgroup owns (4 waves x 32)
 constexpr int kTile = 64;   // rows of the inner-loop tile
