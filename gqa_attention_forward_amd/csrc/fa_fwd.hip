@@ -7,8 +7,7 @@
 // query rows.  The key/value sequence is the inner loop, in tiles of BN = 64 keys
 // ("从零开始写Qwen3", FlashAttention derivation article, section "FlashAttention" and its
 // variant note: Q tiles in parallel, KV as the inner loop).  K and V tiles are staged through
-// LDS, double-buffered per 4-wave group and triple-buffered with 8 waves on 256 rows; Q stays
-// in registers for the whole loop.  The key-split mode (further down) gives one query tile's
+// LDS, double-buffered; Q stays in registers for the whole loop.  The key-split mode (further down) gives one query tile's
 // key tiles to several workgroups and merges their results.
 //
 // Transposed formulation.  The scores are computed as S^T = K Q^T and the output as
@@ -113,9 +112,10 @@ struct SplitParams : Params {
 
 // --------------------------------------------------------------------- kernel
 
-// W waves per workgroup (KG = 1: BM = 32 W query rows).  W = 4: two workgroups share a CU, K
-// and V tiles double-buffered.  W = 8: one workgroup per CU (still two waves per SIMD), tiles
-// triple-buffered so that each load has two tiles of time to land.
+// W waves per workgroup (KG = 1: BM = 32 W query rows).  W = 4: two workgroups share a CU.
+// W = 8: one workgroup per CU (still two waves per SIMD).  K and V tiles are double-buffered:
+// the copies issued at the top of a step land before the step's closing barrier (whose
+// workgroup fence waits for them in any case, so a third buffer would buy no extra lead).
 //
 // KG = 2 (small grids): the W waves form two key groups of W / 2 waves over the same BM =
 // 16 W rows; group k takes the query tile's key tiles k, k + 2, ... with buffers of its own,
@@ -130,7 +130,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     static_assert(KG == 1 || (KG == 2 && !SPLIT), "key groups only in the plain kernel");
     constexpr int WG = W / KG;  // waves of one key group
     constexpr int kBM = 32 * WG, kWaves = WG;
-    constexpr int NBUF = KG == 1 && W == 8 ? 3 : 2;
+    constexpr int NBUF = 2;  // K and V tile buffers of a key group
     constexpr int UNITS = D / 8;                       // 16-byte units per row
     constexpr int KS = D / 16;                         // MFMA k-steps over the head dimension
     constexpr int KB = kBN / 32;                       // 32-key blocks per tile
@@ -139,16 +139,33 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     constexpr bool SWZ = Lds<D>::SWZ;
     constexpr int K_TILE = kBN * KP, V_TILE = kBN * VP;
 
-    // per key group [K buf 0 .. NBUF-1 | V buf 0 .. NBUF-1], then a 1 KiB sink for padding loads
+    // LDS tile buffers.  KG = 1: one LDS object per K buffer, per V buffer and for the 1 KiB
+    // sink of padding loads, so that the compiler can tell a read of one buffer from a copy in
+    // flight into another and does not make the read wait for every copy (with one shared
+    // array it must, the first transposing V read of each step then waiting for the copies
+    // issued at the top of that step).  KG = 2: one array, [K buf 0 .. NBUF-1 | V buf 0 ..
+    // NBUF-1] per key group, then the sink (the group's offset is a run-time value anyway).
     constexpr int GROUP_BYTES = NBUF * (K_TILE + V_TILE);
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[KG * GROUP_BYTES + 1024];
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[KG == 2 ? KG * GROUP_BYTES + 1024 : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char k0_[K_TILE], k1_[K_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char v0_[V_TILE], v1_[V_TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char sink_[1024];
     lds_u8 *smem = (lds_u8 *)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane((tid >> 6) / WG);  // key group
     const int wave = (tid >> 6) % WG;  // wave inside the key group
-    lds_u8 *const gsmem = smem + grp * GROUP_BYTES;  // this group's tile buffers
+    lds_u8 *const gsmem = smem + grp * GROUP_BYTES;  // this group's tile buffers (KG = 2)
+    // K and V buffer i (i a compile-time constant wherever a copy may be in flight)
+    auto kb_ptr = [&](int i) -> lds_u8 * {
+        if constexpr (KG == 1) return i == 0 ? (lds_u8 *)k0_ : (lds_u8 *)k1_;
+        return gsmem + i * K_TILE;
+    };
+    auto vb_ptr = [&](int i) -> lds_u8 * {
+        if constexpr (KG == 1) return i == 0 ? (lds_u8 *)v0_ : (lds_u8 *)v1_;
+        return gsmem + NBUF * K_TILE + i * V_TILE;
+    };
     const int ql = lane & 31;   // query column of this lane inside the wave's 32 rows
     const int hh = lane >> 5;   // which half of each 32-key block this lane holds
 
@@ -227,7 +244,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     constexpr int LOADS_PER_TILE = KI + VI;  // per wave
     static_assert(LOADS_PER_TILE < 16, "wait count encoding");
     constexpr unsigned kPad = 0x7fffff00u;  // an offset past the end of every tile resource
-    lds_u8 *const sink = smem + KG * GROUP_BYTES;
+    lds_u8 *const sink = KG == 1 ? (lds_u8 *)sink_ : smem + KG * GROUP_BYTES;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // key rows at or past kv_end read as zero: the end of the keys, or of this workgroup's share
     // (the pipeline's look-ahead loads run past it)
@@ -258,7 +275,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     };
     auto load_k = [&](int t, int buf) {  // the group's tile t
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, k_rs, t0 + KG * t + grp);
-        lds_u8 *dst = gsmem + buf * K_TILE;
+        lds_u8 *dst = kb_ptr(buf);
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
             const int j = wave_u + kWaves * i;
@@ -267,21 +284,16 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     };
     auto load_v = [&](int t, int buf) {
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, v_rs, t0 + KG * t + grp);
-        lds_u8 *dst = gsmem + NBUF * K_TILE + buf * V_TILE;
+        lds_u8 *dst = vb_ptr(buf);
 #pragma unroll
         for (int i = 0; i < VI; ++i) {
             const int j = wave_u + kWaves * i;
             lds_load16(rs, (lds_void *)(V_INSTR % kWaves == 0 || j < V_INSTR ? dst + j * 1024 : sink), v_src[i]);
         }
     };
-    // this wave's loads into LDS, except the newest `keep` tiles' worth, have landed; a barrier
-    // then publishes them (s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maximum)
-    auto wait_loads = [&](auto keep_tag) {
-        constexpr int n = decltype(keep_tag)::value * LOADS_PER_TILE;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | n);
-    };
-    using Keep0 = std::integral_constant<int, 0>;
-    using Keep1 = std::integral_constant<int, 1>;
+    // every load into LDS this wave issued has landed; a barrier then publishes them
+    // (s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum)
+    auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
     // ---- online-softmax state (A6) and output accumulator
     f32x16 oacc[DB];
@@ -398,8 +410,8 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         constexpr bool QK = decltype(qk_tag)::value;
         float mc = 0.f;  // m * c of tile t, set by the running-max update inside the sequence
         constexpr int J0 = QK ? 0 : NM;  // first MFMA of the sequence
-        const lds_u8 *kp = gsmem + kbuf * K_TILE + k_rd;
-        const lds_u8 *vp = gsmem + NBUF * K_TILE + vbuf * V_TILE + v_rd;
+        const lds_u8 *kp = kb_ptr(kbuf) + k_rd;
+        const lds_u8 *vp = vb_ptr(vbuf) + v_rd;
         if constexpr (QK) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -474,7 +486,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
 
     // scores of one tile only (the first one)
     auto scores = [&](int kbuf, f32x16 (&s)[KB]) {
-        const lds_u8 *kp = gsmem + kbuf * K_TILE + k_rd;
+        const lds_u8 *kp = kb_ptr(kbuf) + k_rd;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -484,62 +496,49 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     };
 
 
-    // Software pipeline over key tiles.  Iteration t reads K_{t+1} (scores of the next tile)
-    // and V_t from LDS, and issues the loads of K_{t+NBUF} and V_{t+NBUF-1} into the buffers
-    // that iteration t-1 finished reading; one barrier per tile publishes the loads issued
-    // NBUF-2 iterations earlier.
+    // Software pipeline over key tiles.  Step t reads K_{t+1} (scores of the next tile) and
+    // V_t from LDS, and issues the loads of K_{t+2} and V_{t+1} into the buffers that step t-1
+    // finished reading; the one barrier per tile publishes them.
     f32x16 s_cur[KB], s_nxt[KB];
     float mt_pending = -INFINITY;  // in-lane max of the scores whose running-max update is pending
     if (n_loc > 0) {
         load_k(0, 0);
         load_v(0, 0);
         load_k(1, 1);
-        if constexpr (NBUF == 3) {
-            load_k(2, 2);
-            load_v(1, 1);
-            wait_loads(Keep1{});
-        } else {
-            wait_loads(Keep0{});
-        }
+        wait_loads();
         __syncthreads();
         scores(0, s_cur);
         mt_pending = mask_max(0, s_cur, t0 + grp < kr.n_full);
         __syncthreads();  // every wave has read K_0 before its buffer is refilled
     }
-    int kb_next = 1 % NBUF, vb_cur = 0, b_load = 0;  // buffers of K_{t+1}, V_t, and of the loads (t % NBUF)
-    auto advance = [&](int &b) { b = b + 1 == NBUF ? 0 : b + 1; };
-    // one full step: probabilities and P V of tile t (scores in cur), scores of tile t+1 into nxt
-    auto body = [&](int t, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
-        load_k(t + NBUF, b_load);  // rows past N (or a tile past the end) read as zero
-        load_v(t + NBUF - 1, (b_load + NBUF - 1) % NBUF);
+    // one full step t: probabilities and P V of tile t (scores in cur), scores of tile t+1 into
+    // nxt.  With ph = t % 2, K_{t+1} and V_t are read from buffers 1 - ph and ph, and the copies
+    // of K_{t+2} and V_{t+1} go to buffers ph and 1 - ph.  ph is a compile-time constant (the
+    // loop below runs steps in pairs), so every buffer is a fixed LDS object.
+    auto body = [&](auto ph_c, int t, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
+        constexpr int ph = decltype(ph_c)::value;
+        load_k(t + 2, ph);  // rows past N (or a tile past the end) read as zero
+        load_v(t + 1, 1 - ph);
         float psum = 0.f;
-        float mt = step(std::true_type{}, kb_next, vb_cur, nxt, cur, mt_pending, psum);
+        float mt = step(std::true_type{}, 1 - ph, ph, nxt, cur, mt_pending, psum);
         l_part += psum;
         if (t0 + KG * (t + 1) + grp >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
         mt_pending = mt;
-        if constexpr (NBUF == 3)
-            wait_loads(Keep1{});
-        else
-            wait_loads(Keep0{});
+        wait_loads();
         __syncthreads();
-        advance(kb_next);
-        advance(vb_cur);
-        advance(b_load);
     };
-    // Full steps come in pairs with the two score arrays swapping roles (no copies); an odd
-    // count starts with one step and one copy.
+    // Steps run in pairs, the two score arrays swapping roles (no copies) as the buffers do;
+    // the second step of a pair sits behind a uniform exit test.
     const int n_steps = n_loc - 1;
-    int t = 0;
-    if (n_steps > 0 && (n_steps & 1)) {
-        body(0, s_cur, s_nxt);
+    for (int t = 0; t < n_steps; t += 2) {
+        body(std::integral_constant<int, 0>{}, t, s_cur, s_nxt);
+        if (t + 1 < n_steps) body(std::integral_constant<int, 1>{}, t + 1, s_nxt, s_cur);
+    }
+    if (n_steps > 0 && (n_steps & 1)) {  // the last tile's scores are in s_nxt
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
-        t = 1;
     }
-    for (; t < n_steps; t += 2) {
-        body(t, s_cur, s_nxt);
-        body(t + 1, s_nxt, s_cur);
-    }
+    const int vb_cur = n_steps > 0 ? n_steps % 2 : 0;  // buffer of the last V tile
     if (n_loc > 0) {  // last tile: no scores to prefetch
         const float mc = update_max(mt_pending);
         probs(s_cur, mc);
@@ -555,7 +554,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         constexpr int NV = DB * 16;
         static_assert((NV + 2) * 64 * WG * 4 <= KG * GROUP_BYTES, "merge area inside the tile buffers");
         const int slot = wave * 64 + lane;
-        wait_loads(Keep0{});  // no load into LDS still in flight (the look-ahead ones included)
+        wait_loads();         // no load into LDS still in flight (the look-ahead ones included)
         __syncthreads();      // and every wave is done with the tile buffers
         if (grp == 1) {
 #pragma unroll
