@@ -682,26 +682,28 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(SplitParams p)
 
 // ------------------------------------------------------------------ host side
 
-// Launch plan: 8-wave workgroups over 256 query rows when they alone fill every CU once,
-// 128-row query tiles otherwise (small grids need the larger workgroup count).  A 128-row
-// grid that leaves CUs with one workgroup at most runs 8-wave workgroups with two key groups
-// when the longest key range has kMinKgTiles tiles or more: with a single 4-wave workgroup
-// on a CU each SIMD runs one wave, and the second group's wave adds throughput (measured
-// about 8 % per key tile with every CU busy, 17 % with 32 workgroups), while the merge and
-// the larger workgroup add a fixed cost (about 2 us) that short key ranges do not win back.
+// Launch plan: at D = 128, 8-wave workgroups over 256 query rows when they alone fill every
+// CU once; 128-row query tiles otherwise -- small grids need the larger workgroup count, and
+// at D = 64 two independent 4-wave workgroups per CU measured 7-8 % faster than one 8-wave
+// workgroup.  A 128-row grid that leaves CUs with one workgroup at most runs 8-wave
+// workgroups with two key groups when the longest key range has kMinKgTiles tiles or more:
+// with a single 4-wave workgroup on a CU each SIMD runs one wave, and the second group's wave
+// adds throughput (measured about 8 % per key tile with every CU busy, 17 % with 32
+// workgroups), while the merge and the larger workgroup add a fixed cost (about 2 us) that
+// short key ranges do not win back.
 constexpr int kNumCUs = 256;      // compute units of an MI355X
 constexpr int kMinKgTiles = 16;   // key tiles of the longest range for two key groups
 struct LaunchShape {
     int W;   // waves per workgroup
     int KG;  // key groups
 };
-static bool tiles_256(int B, int Hq, int M)
+static bool tiles_256(int B, int Hq, int M, int D)
 {
-    return (long long)B * Hq * ((M + 255) / 256) >= kNumCUs;
+    return D == 128 && (long long)B * Hq * ((M + 255) / 256) >= kNumCUs;
 }
-static LaunchShape launch_shape(int B, int Hq, int M, int N)
+static LaunchShape launch_shape(int B, int Hq, int M, int N, int D)
 {
-    if (tiles_256(B, Hq, M)) return {8, 1};
+    if (tiles_256(B, Hq, M, D)) return {8, 1};
     const long long wg128 = (long long)B * Hq * ((M + 127) / 128);
     // the longest key range of any query tile is the whole key sequence (the last tile's, when causal)
     if (wg128 <= kNumCUs && (N + kBN - 1) / kBN >= kMinKgTiles) return {8, 2};
@@ -711,7 +713,7 @@ static LaunchShape launch_shape(int B, int Hq, int M, int N)
 static int tile_shape(int B, int Hq, int M, int D, int *BM, int *BN)
 {
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-    *BM = tiles_256(B, Hq, M) ? 256 : 128;
+    *BM = tiles_256(B, Hq, M, D) ? 256 : 128;
     *BN = kBN;
     return FA_OK;
 }
@@ -963,7 +965,7 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
     if (p.total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;  // one-dimensional grid limit
 
     hipStream_t s = (hipStream_t)stream;
-    const fa::LaunchShape ls = fa::launch_shape(B, Hq, M, N);
+    const fa::LaunchShape ls = fa::launch_shape(B, Hq, M, N, D);
     hipError_t err = dtype == FA_F16 ? fa::launch_t<_Float16>(p, D, ls, causal != 0, s)
                                      : fa::launch_t<__bf16>(p, D, ls, causal != 0, s);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

@@ -193,8 +193,9 @@ int fa_fwd_splitkv_strided(const void *q, const void *k, const void *v, void *o,
  * counts and benchmarks can count the work actually issued.
  *
  * fa_tile_shape: the query-tile and key-tile heights fa_fwd uses for a problem with B batches,
- *   Hq query heads, M queries per head and head dimension D (query tiles of 256 rows when the
- *   grid still fills the GPU, 128 rows otherwise; key tiles of 64 rows).  Returns FA_OK,
+ *   Hq query heads, M queries per head and head dimension D (query tiles of 256 rows when
+ *   D = 128 and the grid still fills the GPU, 128 rows otherwise; key tiles of 64 rows).
+ *   Returns FA_OK,
  *   FA_ERR_INVALID_ARG for a null pointer or non-positive size, FA_ERR_UNSUPPORTED for an
  *   unsupported D.
  *

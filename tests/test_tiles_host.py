@@ -68,12 +68,14 @@ def test_classification_matches_brute_force(M, N, BM, BN, causal):
 
 
 def test_tile_shape():
-    # 8-wave workgroups (256 rows) once they alone fill the 256 CUs, 4-wave ones below that
+    # 8-wave workgroups (256 rows) at D = 128 once they alone fill the 256 CUs, 4-wave ones
+    # (128 rows) below that and at D = 64
     assert fa.fa_tile_shape(1, 32, 16384, 128) == (256, 64)
     assert fa.fa_tile_shape(8, 32, 4096, 128) == (256, 64)
     assert fa.fa_tile_shape(4, 32, 512, 128) == (256, 64)
     assert fa.fa_tile_shape(2, 16, 1024, 128) == (128, 64)
     assert fa.fa_tile_shape(1, 2, 128, 64) == (128, 64)
+    assert fa.fa_tile_shape(1, 32, 16384, 64) == (128, 64)  # D = 64: 4-wave workgroups on any grid
     with pytest.raises(fa.FaError):
         fa.fa_tile_shape(1, 2, 128, 96)
     with pytest.raises(fa.FaError):
