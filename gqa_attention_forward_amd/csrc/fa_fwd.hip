@@ -7,8 +7,8 @@
 // query rows.  The key/value sequence is the inner loop, in tiles of BN = 64 keys
 // ("从零开始写Qwen3", FlashAttention derivation article, section "FlashAttention" and its
 // variant note: Q tiles in parallel, KV as the inner loop).  K and V tiles are staged through
-// LDS, double-buffered; Q stays in registers for the whole loop.  The key-split mode (further down) gives one query tile's
-// key tiles to several workgroups and merges their results.
+// LDS, double-buffered; Q stays in registers for the whole loop.  The key-split mode (further
+// down) gives one query tile's key tiles to several workgroups and merges their results.
 //
 // Transposed formulation.  The scores are computed as S^T = K Q^T and the output as
 // O^T = V^T P^T on the 32x32x16 MFMA, so the MFMA accumulator's column index -- which is
@@ -144,7 +144,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     // flight into another and does not make the read wait for every copy (with one shared
     // array it must, the first transposing V read of each step then waiting for the copies
     // issued at the top of that step).  KG = 2: one array, [K buf 0 .. NBUF-1 | V buf 0 ..
-    // NBUF-1] per key group, then the sink (the group's offset is a run-time value anyway).
+    // NBUF-1] per key group, then the sink -- separate objects measured slower there.
     constexpr int GROUP_BYTES = NBUF * (K_TILE + V_TILE);
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[KG == 2 ? KG * GROUP_BYTES + 1024 : 16];
     __shared__ __attribute__((aligned(16))) unsigned char k0_[K_TILE], k1_[K_TILE];
