@@ -13,9 +13,11 @@
 //   dQ:    one workgroup per (b, h, 128 query rows), lane = query (as in the forward): per
 //          64-key tile, S^T = K Q^T and dP^T = V dO^T with Q and dO resident in registers,
 //          dS^T from them, then dQ^T += K^T dS^T with K^T read by the transposing LDS read.
-//   dK/dV: one workgroup per (b, kv head, 128 keys), lane = key, K and V resident in
-//          registers: per 64-query tile of every query head of the group, S = Q K^T and
-//          dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (transposing reads of dO and Q).
+//   dK/dV: one workgroup per (b, kv head, 128 keys), lane = key, K resident in registers and
+//          the block's V rows in LDS: per 32-query tile of every query head of the group,
+//          S = Q K^T and dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS (transposing
+//          reads of dO and Q).  V in LDS rather than registers leaves room for the operand
+//          read-ahead without spills; the 32-row query tiles keep two workgroups' LDS per CU.
 // No atomics: every output element has one owner, so results are deterministic.
 // Each wave raises its priority (s_setprio 1) while it issues a run of MFMAs and drops it for the
 // exp / dS arithmetic between them, so that the other wave on the SIMD fills the VALU while the
@@ -98,16 +100,16 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p)
 
 // ------------------------------------------------------------ tile loads
 
-// HBM -> LDS copy of one 64-row tile of a contiguous [rows, D] slab into the swizzled layout:
+// HBM -> LDS copy of ROWS rows of a contiguous [rows, D] slab into the swizzled layout:
 // instruction j (of TI) fills LDS bytes [1 KiB j, 1 KiB (j+1)); the wave issues j = wave + 4 i.
 // Lane l's slot is row j * RPK + l / UPR, physical unit l % UPR; it gathers the logical unit
 // (l % UPR) ^ swz(row).  swz depends only on row bits that j = wave + 4 i does not change, so
-// one source offset per lane serves every i (plus i * 16 KiB / TI rows).
-template <int D> struct TileLoad {
+// one source offset per lane serves every i (plus i * 4 RPK rows).
+template <int D, int ROWS> struct TileLoad {
     static constexpr int RB = 2 * D;                // bytes per row
     static constexpr int UPR = RB / 16;             // units per row
     static constexpr int RPK = 1024 / RB;           // rows per 1 KiB instruction
-    static constexpr int TI = kTile * RB / 1024;    // instructions per tile
+    static constexpr int TI = ROWS * RB / 1024;     // instructions per tile
     static constexpr int PER_WAVE = TI / 4;
     static_assert(PER_WAVE * 4 == TI, "tile instructions split over 4 waves");
     unsigned src;
@@ -116,10 +118,10 @@ template <int D> struct TileLoad {
         const int row = wave * RPK + lane / UPR, phys = lane % UPR;
         src = (unsigned)(row * RB + ((phys ^ swz<D>(row)) * 16));
     }
-    // rows [r0, r0 + 64) of the slab at base, valid rows < rows_valid
+    // rows [r0, r0 + ROWS) of the slab at base, valid rows < rows_valid
     __device__ __forceinline__ void issue(const void *base, int r0, int rows_valid, lds_u8 *dst, int wave) const
     {
-        const int rows = rows_valid - r0 < kTile ? rows_valid - r0 : kTile;
+        const int rows = rows_valid - r0 < ROWS ? rows_valid - r0 : ROWS;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const char *)base + (long long)r0 * RB), (short)0, rows > 0 ? rows * RB : 0, 0x00020000);
 #pragma unroll
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    const TileLoad<D> ld(wave, lane);
+    const TileLoad<D, kTile> ld(wave, lane);
     const TrOffsets<D> tro(lane);
     const int n_tiles = kr.n_tiles;
     if (n_tiles > 0) {
@@ -277,10 +279,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
 {
-    constexpr int KS = D / 16, DB = D / 32, TILE = kTile * 2 * D;
-    constexpr int BUF = 2 * TILE + 1024;  // Q tile, dO tile, stats chunk (512 bytes used)
+    constexpr int KS = D / 16, DB = D / 32, QT = 32;  // QT: query rows per step
+    constexpr int TILE = QT * 2 * D;
+    constexpr int BUF = 2 * TILE + 1024;  // Q tile, dO tile, stats (32 lse, 32 Delta; the
+                                          // copy writes 16 bytes per lane of the wave: 1 KiB)
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * BUF];
-    lds_u8 *smem = (lds_u8 *)smem_raw;
+    __shared__ __attribute__((aligned(16))) unsigned char vt_[kRows * 2 * D];  // V of the block
+    lds_u8 *smem = (lds_u8 *)smem_raw, *vtile = (lds_u8 *)vt_;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kl = lane & 31, hh = lane >> 5;
 
@@ -295,17 +300,14 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
     const int key = n0 + wave * 32 + kl;
     const bool kvalid = key < N;
 
-    // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
-    u32x4 kreg[KS], vreg[KS];
+    // K row of this lane's key: B operand of S = Q K^T (the V rows, B operands of dP = dO V^T,
+    // are read from the block's V tile in LDS)
+    u32x4 kreg[KS];
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
         const T *kr = (const T *)p.k + (bhk * N + key) * (size_t)D + hh * 8;
-        const T *vr = (const T *)p.v + (bhk * N + key) * (size_t)D + hh * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kreg[ks] = kvalid ? *(const u32x4 *)(kr + ks * 16) : z;
-            vreg[ks] = kvalid ? *(const u32x4 *)(vr + ks * 16) : z;
-        }
+        for (int ks = 0; ks < KS; ++ks) kreg[ks] = kvalid ? *(const u32x4 *)(kr + ks * 16) : z;
     }
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -314,30 +316,38 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
         for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
 
     // query tiles that see some key of the block: i >= n0 - (N - M) when causal
-    const int n_qtiles = (M + kTile - 1) / kTile;
+    const int n_qtiles = (M + kTile - 1) / kTile;  // 64-row chunks of the statistics workspace
+    const int n_q32 = (M + QT - 1) / QT;
     int qt_lo = 0;
     if (CAUSAL) {
         const long long first = (long long)n0 - (N - M);
-        qt_lo = first <= 0 ? 0 : (first >= M ? n_qtiles : (int)(first / kTile));
+        qt_lo = first <= 0 ? 0 : (first >= M ? n_q32 : (int)(first / QT));
     }
-    const int nq = n_qtiles - qt_lo;
+    const int nq = n_q32 - qt_lo;
     const int iters = g * nq;
     const float c = p.c;
     const long long diag = (long long)n0 + kRows - 1 - (N - M);  // rows >= diag see every key of the block
 
-    const TileLoad<D> ld(wave, lane);
+    const TileLoad<D, QT> ld(wave, lane);
     const TrOffsets<D> tro(lane);
+    {  // the block's V rows, once (landed by the first step's wait)
+        const TileLoad<D, kRows> vl(wave, lane);
+        vl.issue((const T *)p.v + bhk * N * D, n0, N, vtile, wave);
+    }
     auto issue = [&](int it, int buf) {
         const int h = hk * g + it / nq, qt = qt_lo + it % nq;
         const size_t bh = (size_t)b * p.Hq + h;
         lds_u8 *dst = smem + buf * BUF;
-        ld.issue((const T *)p.q + bh * M * D, qt * kTile, M, dst, wave);
-        ld.issue((const T *)p.dout + bh * M * D, qt * kTile, M, dst + TILE, wave);
-        if (wave == 0) {  // the 512-byte stats chunk: lanes 0..31, the others read zeros
-            const float *st = p.stats + (bh * n_qtiles + qt) * kStats;
+        ld.issue((const T *)p.q + bh * M * D, qt * QT, M, dst, wave);
+        ld.issue((const T *)p.dout + bh * M * D, qt * QT, M, dst + TILE, wave);
+        if (wave == 0) {  // 32 lse (lanes 0..7) and 32 Delta (lanes 8..15) of this 32-row tile
+            const int i0 = qt * QT, ch = i0 / kTile, half = (i0 % kTile) / QT;
+            const float *st = p.stats + (bh * n_qtiles + ch) * kStats + half * QT;
             const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void *)st, (short)0, kStats * 4, 0x00020000);
-            lds_load16(rs, (lds_void *)(dst + 2 * TILE), lane < 32 ? (unsigned)(lane * 16) : 0x7fffff00u);
+                __builtin_amdgcn_make_buffer_rsrc((void *)st, (short)0, (kTile + QT) * 4, 0x00020000);
+            const unsigned off = lane < 8 ? (unsigned)(lane * 16) : lane < 16 ? (unsigned)(kTile * 4 + (lane - 8) * 16)
+                                                                             : 0x7fffff00u;
+            lds_load16(rs, (lds_void *)(dst + 2 * TILE), off);
         }
     };
     if (iters > 0) issue(0, 0);
@@ -347,79 +357,74 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
         __syncthreads();
         if (it + 1 < iters) issue(it + 1, buf ^ 1);
         const int qt = qt_lo + it % nq;
-        const int i0 = qt * kTile;
-        const bool masked = n0 + kRows > N || i0 + kTile > M || (CAUSAL && i0 < diag);  // uniform
+        const int i0 = qt * QT;
+        const bool masked = n0 + kRows > N || i0 + QT > M || (CAUSAL && i0 < diag);
         const lds_u8 *qtile = smem + buf * BUF, *dtile = qtile + TILE;
         const float *stl = (const float *)(qtile + 2 * TILE);
-#pragma unroll 1
-        for (int qb = 0; qb < 2; ++qb) {
-            f32x16 s, dp;
+        f32x16 s, dp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = Elem<T>::mfma(read_row<D>(qtile, qb * 32 + kl, 2 * ks + hh), kreg[ks], s);
-                dp = Elem<T>::mfma(read_row<D>(dtile, qb * 32 + kl, 2 * ks + hh), vreg[ks], dp);
-            }
-            __builtin_amdgcn_s_setprio(0);
-            // register r is query i0 + 32 qb + 8 (r/4) + 4 hh + r%4 of this lane's key; P replaces
-            // S and dS replaces dP in place
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int qi = qb * 32 + 8 * gq + 4 * hh;
-                const f32x4 l4 = *(const f32x4 *)(stl + qi);
-                const f32x4 d4 = *(const f32x4 *)(stl + kTile + qi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * gq + e;
-                    float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
-                    if (masked) {
-                        const int i = i0 + qi + e;
-                        x = kvalid && i < M && (!CAUSAL || key <= i + (N - M)) ? x : 0.f;
-                    }
-                    s[r] = x;
-                    dp[r] = x * (dp[r] - d4[e]);
+        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+        __builtin_amdgcn_s_setprio(1);
+        // MFMA m: k-step m / 2 of S (m even: Q rows by the K registers) or of dP (m odd: dO rows
+        // by this lane's V row, both from LDS); operands read kReadAhead MFMAs ahead
+        mfma_run2<2 * KS, kReadAhead>(
+            [&](auto mc, u32x4 &a, u32x4 &bo) {
+                constexpr int m = decltype(mc)::value, ks = m / 2;
+                if constexpr (m % 2 == 0) {
+                    a = read_row<D>(qtile, kl, 2 * ks + hh);
+                } else {
+                    a = read_row<D>(dtile, kl, 2 * ks + hh);
+                    bo = read_row<D>(vtile, wave * 32 + kl, 2 * ks + hh);
                 }
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries
-            __builtin_amdgcn_s_setprio(1);
-            if constexpr (CAUSAL) {
-                // transposing reads issued kReadAhead MFMAs ahead (1-6 % faster on the causal
-                // shapes; the non-causal kernel spilled inside the loop with it and ran 2-4 %
-                // slower, so it keeps the plain loop below).
-                // MFMA m: k-step tt = m / (2 DB) of column block db = (m / 2) % DB, of dV (m even,
-                // dO^T by P) or of dK (m odd, Q^T by dS)
-                u32x4 bp = pack_b<T>(s, 0), bs = pack_b<T>(dp, 0);
-                mfma_run<4 * DB, kReadAhead>(
-                    [&](auto mc) {
-                        constexpr int m = decltype(mc)::value;
-                        return read_tr<D>(m % 2 ? qtile : dtile, tro, qb * 32 + 16 * (m / (2 * DB)), (m / 2) % DB);
-                    },
-                    [&](auto mc, const u32x4 &a) {
-                        constexpr int m = decltype(mc)::value, db = (m / 2) % DB;
-                        if constexpr (m == 2 * DB) {
-                            bp = pack_b<T>(s, 1);
-                            bs = pack_b<T>(dp, 1);
-                        }
-                        if constexpr (m % 2 == 0)
-                            dv[db] = Elem<T>::mfma(a, bp, dv[db]);
-                        else
-                            dk[db] = Elem<T>::mfma(a, bs, dk[db]);
-                    });
-            } else {
+            },
+            [&](auto mc, const u32x4 &a, const u32x4 &bo) {
+                constexpr int m = decltype(mc)::value;
+                if constexpr (m % 2 == 0)
+                    s = Elem<T>::mfma(a, kreg[m / 2], s);
+                else
+                    dp = Elem<T>::mfma(a, bo, dp);
+            });
+        __builtin_amdgcn_s_setprio(0);
+        // register r is query i0 + 8 (r/4) + 4 hh + r%4 of this lane's key; P replaces S and dS
+        // replaces dP in place
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const u32x4 bp = pack_b<T>(s, tt), bs = pack_b<T>(dp, tt);
+        for (int gq = 0; gq < 4; ++gq) {
+            const int qi = 8 * gq + 4 * hh;
+            const f32x4 l4 = *(const f32x4 *)(stl + qi);
+            const f32x4 d4 = *(const f32x4 *)(stl + QT + qi);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        dv[db] = Elem<T>::mfma(read_tr<D>(dtile, tro, qb * 32 + 16 * tt, db), bp, dv[db]);
-                        dk[db] = Elem<T>::mfma(read_tr<D>(qtile, tro, qb * 32 + 16 * tt, db), bs, dk[db]);
-                    }
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * gq + e;
+                float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
+                if (masked) {
+                    const int i = i0 + qi + e;
+                    x = kvalid && i < M && (!CAUSAL || key <= i + (N - M)) ? x : 0.f;
                 }
+                s[r] = x;
+                dp[r] = x * (dp[r] - d4[e]);
             }
-            __builtin_amdgcn_s_setprio(0);
         }
+        // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries.  MFMA m: k-step
+        // tt = m / (2 DB) of column block db = (m / 2) % DB, of dV (m even) or dK (m odd)
+        __builtin_amdgcn_s_setprio(1);
+        u32x4 bp = pack_b<T>(s, 0), bs = pack_b<T>(dp, 0);
+        mfma_run<4 * DB, kReadAhead>(
+            [&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                return read_tr<D>(m % 2 ? qtile : dtile, tro, 16 * (m / (2 * DB)), (m / 2) % DB);
+            },
+            [&](auto mc, const u32x4 &a) {
+                constexpr int m = decltype(mc)::value, db = (m / 2) % DB;
+                if constexpr (m == 2 * DB) {
+                    bp = pack_b<T>(s, 1);
+                    bs = pack_b<T>(dp, 1);
+                }
+                if constexpr (m % 2 == 0)
+                    dv[db] = Elem<T>::mfma(a, bp, dv[db]);
+                else
+                    dk[db] = Elem<T>::mfma(a, bs, dk[db]);
+            });
+        __builtin_amdgcn_s_setprio(0);
     }
     if (kvalid) {
         T *dkr = (T *)p.dk + (bhk * N + key) * (size_t)D + hh * 16;

@@ -38,4 +38,23 @@ __device__ __forceinline__ void mfma_run(Read &&read, Mfma &&mfma)
     });
 }
 
+// The same with both operands from LDS where needed: read(m, a, b) fills the operand(s) of
+// MFMA m that come from LDS (a, and b when the other is not a register).
+template <int N, int RA, typename Read, typename Mfma>
+__device__ __forceinline__ void mfma_run2(Read &&read, Mfma &&mfma)
+{
+    u32x4 a[RA + 1], b[RA + 1];
+    static_for<0, RA>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        read(mc, a[m], b[m]);
+    });
+    static_for<0, N>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m + RA < N)
+            read(std::integral_constant<int, m + RA>{}, a[(m + RA) % (RA + 1)], b[(m + RA) % (RA + 1)]);
+        mfma(mc, a[m % (RA + 1)], b[m % (RA + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
 }  // namespace fa
