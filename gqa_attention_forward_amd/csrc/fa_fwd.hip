@@ -748,6 +748,7 @@ constexpr int kSplitBM = 128;
 // largest K/V row stride (elements): a key tile's 32-bit buffer range must hold 63 rows plus one
 constexpr long long kMaxKvRowStride = ((0x7fff0000LL / 2) - 128) / 63;
 constexpr int kSplitTargetWgs = 512;  // two 4-wave workgroups per CU
+constexpr int kSplitMinWgs = 256;     // one per CU
 constexpr int kSplitMinTiles = 8;     // smallest share the automatic plan hands one workgroup
 constexpr int kSplitMinRange = 32;    // the automatic plan splits only query tiles this long or longer
 
@@ -763,7 +764,11 @@ struct SplitPlan {
 // plain 4-wave grid already has kSplitTargetWgs workgroups or no query tile visits
 // kSplitMinRange key tiles (the partial results' round trip and the merge launch would cost
 // more than the balance gains), else the total key-tile work spread over about
-// kSplitTargetWgs workgroups, at least kSplitMinTiles tiles each.
+// kSplitTargetWgs workgroups, at least kSplitMinTiles tiles each.  A share's partial output
+// (slot_rows fp32 rows, written once and read once by the merge) costs slot_rows / 32 key
+// tiles of K/V bytes, so shares are also made at least slot_rows / 4 tiles long (that round
+// trip then adds at most 1/8 to the share's traffic), as long as the grid keeps one
+// workgroup per CU.
 static int split_plan(int B, int Hq, int Hkv, int M, int N, int D, bool causal, int tiles, SplitPlan *pl)
 {
     // short queries: stack the query heads of a KV group into the rows of one unit
@@ -782,11 +787,17 @@ static int split_plan(int B, int Hq, int Hkv, int M, int N, int D, bool causal, 
         if (nt[r] > max_tiles) max_tiles = nt[r];
     }
     const long long heads = (long long)B * Hq / pack;  // units
+    const int slot_rows = R < kSplitBM ? R : kSplitBM;
     if (tiles <= 0) {
         if (heads * n_qt >= kSplitTargetWgs || max_tiles < kSplitMinRange) {
             tiles = max_tiles;
         } else {
-            const long long t = (heads * total_tiles + kSplitTargetWgs - 1) / kSplitTargetWgs;
+            const long long work = heads * total_tiles;
+            const long long t_target = (work + kSplitTargetWgs - 1) / kSplitTargetWgs;
+            const long long t_cus = (work + kSplitMinWgs - 1) / kSplitMinWgs;
+            const long long t_rows = (slot_rows + 3) / 4;
+            long long t = t_rows < t_cus ? t_rows : t_cus;
+            if (t < t_target) t = t_target;
             tiles = (int)(t < kSplitMinTiles ? kSplitMinTiles : (t > max_tiles ? max_tiles : t));
         }
     }
@@ -806,7 +817,7 @@ static int split_plan(int B, int Hq, int Hkv, int M, int N, int D, bool causal, 
     sp.slots = sp.prefix[sp.n_split_ranks];
     sp.causal = causal ? 1 : 0;
     sp.pack = pack;
-    sp.slot_rows = R < kSplitBM ? R : kSplitBM;
+    sp.slot_rows = slot_rows;
     sp.total = heads * sp.wg_per_head;
     pl->tiles = tiles;
     const size_t rows = (size_t)heads * sp.slots * sp.slot_rows;

@@ -159,7 +159,8 @@ const char *fa_strerror(int code);
  * fa_splitkv_plan: host-only.  tiles_per_split > 0 is used as given; <= 0 asks for the automatic
  *   choice (no split when the 4-wave grid already has 512 workgroups or no query tile visits 32
  *   key tiles, else shares of the key-tile work spread over about 512 workgroups, at least 8
- *   tiles each).  Writes the key tiles per share
+ *   tiles each, and at least a quarter of the rows a share's partial output holds as long as
+ *   the grid keeps 256 workgroups).  Writes the key tiles per share
  *   actually used (*tiles_used), the workgroup count of the split kernel (*workgroups) and the
  *   workspace size in bytes (*workspace_bytes; 0 when no query tile is split).  Returns FA_OK,
  *   FA_ERR_INVALID_ARG (null pointer, non-positive size, Hq % Hkv != 0) or FA_ERR_UNSUPPORTED

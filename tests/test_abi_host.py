@@ -114,6 +114,16 @@ def test_splitkv_auto_policy():
     assert used == 8 and wgs == 4
     used, wgs, ws = fa.fa_splitkv_plan(1, 2, 2, 64, 2048, 64, False, 0)  # no grouping: one tile per head
     assert used == 8 and wgs == 2 * 4
+    # full 128-row tiles (64-row chunk x 4 stacked heads): a share's fp32 partial output weighs as
+    # much as 4 key tiles, so shares grow to 32 tiles while the grid keeps 256 workgroups
+    used, wgs, ws = fa.fa_splitkv_plan(4, 32, 8, 64, 8192, 128, True, 0)
+    assert used == 32 and wgs == 4 * 8 * 2 * 4
+    # decode with few rows per tile keeps the 512-workgroup spread
+    used, wgs, ws = fa.fa_splitkv_plan(8, 32, 8, 1, 8192, 128, True, 0)
+    assert used == 16 and wgs == 8 * 8 * 8
+    # one 128-row tile on a small grid: the CU bound wins over the partial-output bound
+    used, wgs, ws = fa.fa_splitkv_plan(1, 8, 8, 128, 8192, 128, False, 0)
+    assert used == 8 and wgs == 8 * 16
 
 
 SPLIT_GOOD = dict(GOOD, tiles=1, ws=0x100000, ws_bytes=1 << 30)
