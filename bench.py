@@ -343,8 +343,8 @@ def cpu_baseline(w, q, k, v, target_s):
         "unit": "TFLOPS",
         "cores": oracle.threads_used(),
         "kind": "oracle",
-        "sample": f"{n} random query rows (of {total_rows}) of {w.name}, all their visible keys; "
-                  f"{fl / 1e9:.1f} GFLOP causal-adjusted in {dt:.1f} s, fp64",
+        "sample": (f"all {total_rows} query rows" if n == total_rows else f"{n} random query rows (of {total_rows})")
+                  + f" of {w.name}, all their visible keys; {fl / 1e9:.1f} GFLOP causal-adjusted in {dt:.1f} s, fp64",
     }
 
 
