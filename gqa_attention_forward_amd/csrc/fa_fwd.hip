@@ -421,10 +421,14 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         u32x4 a[RA + 1];
 #pragma unroll
         for (int j = J0; j < J0 + RA; ++j) a[j % (RA + 1)] = read_op(j, kp, vp);
+        // the wave issuing the score half of a step (its exp2 work) takes issue priority over
+        // a wave in its value half, which keeps the two waves of a SIMD half a step apart
+        if constexpr (QK) __builtin_amdgcn_s_setprio(1);
         float mt = -INFINITY;
         u32x4 bop[2];
 #pragma unroll
         for (int j = J0; j < 2 * NM; ++j) {
+            if (j == NM) __builtin_amdgcn_s_setprio(0);
             if (j + RA < 2 * NM) a[(j + RA) % (RA + 1)] = read_op(j + RA, kp, vp);
             if (j < NM) {
                 s_next[j % KB] = Elem<T>::mfma(a[j % (RA + 1)], qreg[j / KB], s_next[j % KB]);
