@@ -103,6 +103,16 @@ def roofline(w, flops, avg_ms, traffic):
             "frac": round(achieved / peak, 4), "traffic": traffic, "kernel_avg_us": round(avg_ms * 1e3, 3)}
 
 
+def step_stats(durs):
+    """Per-launch kernel times (ms, in launch order): median, min and mean, and the means of the
+    first and last five launches, so that a clock still ramping up during the timed steps shows."""
+    srt = sorted(durs)
+    n5 = min(5, len(durs))
+    return {"median": round(srt[len(srt) // 2], 4), "min": round(srt[0], 4),
+            "mean": round(sum(durs) / len(durs), 4),
+            "mean_first5": round(sum(durs[:n5]) / n5, 4), "mean_last5": round(sum(durs[-n5:]) / n5, 4)}
+
+
 # workloads whose inputs fit in the 256 MB last-level cache (the small parity shapes)
 SMALL_CACHE_RESIDENT = ("tiny_causal_gqa", "pages_causal_gqa_1k")
 
@@ -141,7 +151,7 @@ def time_gpu(fa, w, q, k, v, steps, warmup, split_kv="auto", min_warm_s=0.0):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms, in launch order
     return wall, durs, o, lse
 
 
@@ -218,7 +228,7 @@ def time_gpu_bwd(fa, w, q, k, v, steps, warmup, min_warm_s=0.0):
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
+    durs = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]  # ms, in launch order
     return wall, durs, grads[0], lse
 
 
@@ -295,8 +305,15 @@ def run_gdn(args, fa, w):
     }
 
 
-def cpu_baseline(w, q, k, v, target_s):
-    """Times the oracle (as it stands) on a random sample of rows of the workload."""
+# parity bar of the timed output against the oracle's rows: max-abs error of O, and of lse
+O_TOL = {"f16": 4e-3, "bf16": 1.6e-2}
+LSE_TOL = 1e-3
+
+
+def cpu_baseline(w, q, k, v, target_s, o=None, lse=None):
+    """Times the oracle (as it stands) on a random sample of rows of the workload.  When the timed
+    GPU output (o, lse) is given, the same rows of it are compared with the oracle's: the errors go
+    into the report, and a result outside the parity bar ends the benchmark with an error."""
     import numpy as np
 
     import oracle
@@ -332,13 +349,13 @@ def cpu_baseline(w, q, k, v, target_s):
     for attempt in range(2):
         rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.attn_fwd_rows(qc, kc, vc, w.scale, w.causal, rows)
+        ro, rlse = oracle.attn_fwd_rows(qc, kc, vc, w.scale, w.causal, rows)
         dt = time.perf_counter() - t0
         fl = flops_of(rows)
         if dt >= 0.6 * target_s or n == total_rows or attempt == 1:
             break
         n = int(min(total_rows, n * target_s / max(dt, 1e-3)))
-    return {
+    out = {
         "value": fl / dt / 1e12,
         "unit": "TFLOPS",
         "cores": oracle.threads_used(),
@@ -346,6 +363,21 @@ def cpu_baseline(w, q, k, v, target_s):
         "sample": (f"all {total_rows} query rows" if n == total_rows else f"{n} random query rows (of {total_rows})")
                   + f" of {w.name}, all their visible keys; {fl / 1e9:.1f} GFLOP causal-adjusted in {dt:.1f} s, fp64",
     }
+    if o is not None:
+        import torch
+
+        idx = torch.from_numpy(rows)
+        og = o.reshape(-1, w.D)[idx.to(o.device)].double().cpu().numpy()
+        lg = lse.reshape(-1)[idx.to(lse.device)].double().cpu().numpy()
+        fin = np.isfinite(rlse)
+        err_o = float(np.abs(og - ro).max())
+        err_l = float(np.abs(lg[fin] - rlse[fin]).max()) if fin.any() else 0.0
+        tol = O_TOL["bf16" if w.dtype == torch.bfloat16 else "f16"]
+        ok = (np.isfinite(og).all() and err_o <= tol and err_l <= LSE_TOL and np.all(np.isneginf(lg[~fin]))
+              and np.all(og[~fin] == 0.0))
+        out["check"] = {"rows": int(rows.size), "max_abs_err_o": err_o, "tol_o": tol, "max_abs_err_lse": err_l,
+                        "tol_lse": LSE_TOL, "ok": bool(ok)}
+    return out
 
 
 def calibrate_copy(nbytes: int):
@@ -415,6 +447,8 @@ def main():
         flops = accounting.workload_flops(w) * (2.5 if args.which == "bwd" else 1.0)
         tflops = flops * args.steps / wall / 1e12
         avg_ms = sum(durs) / len(durs)
+        stats = step_stats(durs)
+        durs = sorted(durs)
         achieved = flops / (avg_ms * 1e-3) / 1e12
         bm, bn = fa.fa_tile_shape(w.B, w.Hq, w.M, w.D)
         f_, m_, _ = fa.fa_tile_counts(w.M, w.N, bm, bn, w.causal)
@@ -457,14 +491,20 @@ def main():
                            "causal": w.causal, "seed": w.seed, "peaky_k_rows": w.peak_rate,
                            "parallelism": "single GPU"},
                 "pct_of_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 3),
+                "step_ms": stats,
                 "roofline": roofline(w, flops, avg_ms, traffic),
                 "cpu_baseline": None,
             }
             if not args.no_cpu_baseline and args.which == "fwd":
-                result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+                result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, o, lse)
         del q, k, v, o, lse
         torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
+    chk = (result.get("cpu_baseline") or {}).get("check") if result else None
+    if chk is not None and not chk["ok"]:
+        print(f"bench.py: the timed output disagrees with the oracle on {chk['rows']} sampled rows: {chk}",
+              file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -298,21 +298,42 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
+def _expect_all(specs):
+    """Checks tensor arguments against the sizes and element type the C ABI will be told.
+    specs: (name, tensor, shape, dtype) tuples; the first tensor's device is the reference.  All
+    shapes, then dtypes and contiguity, are checked before any device check (a tensor smaller
+    than the sizes passed would send the kernels past its allocation), then that every tensor is
+    a device tensor on the first one's device."""
+    for name, t, shape, dtype in specs:
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    for name, t, shape, dtype in specs:
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    device = specs[0][1].device
+    for name, t, shape, dtype in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, stream=None):
     """dq, dk, dv for contiguous device tensors: q, dout, o [B,Hq,M,D], k, v [B,Hkv,N,D] (fp16/bf16)
     and lse [B,Hq,M] fp32 from attention_forward on the same inputs.  The workspace comes from
     torch's caching allocator; kernels are enqueued on `stream` (default: the current stream)."""
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D: q [B, Hq, M, D], k [B, Hkv, N, D]")
     B, Hq, M, D = q.shape
-    _, Hkv, N, _ = k.shape
-    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(v.shape) != tuple(k.shape):
-        raise ValueError("shape mismatch")
-    if tuple(lse.shape) != (B, Hq, M) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 [B, Hq, M]")
+    Hkv, N = k.shape[1], k.shape[2]
+    _dtype_code(q)  # fp16 or bf16
+    _expect_all([("q", q, (B, Hq, M, D), q.dtype), ("k", k, (B, Hkv, N, D), q.dtype),
+                 ("v", v, (B, Hkv, N, D), q.dtype), ("o", o, (B, Hq, M, D), q.dtype),
+                 ("dout", dout, (B, Hq, M, D), q.dtype), ("lse", lse, (B, Hq, M), torch.float32)])
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if stream is None:
@@ -338,15 +359,18 @@ def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, s
     Returns (o [B,T,Hv,DV], final state [B,Hv,128,DV] fp32, A)."""
     import torch
 
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be 4-D: q [B, T, Hqk, 128], v [B, T, Hv, DV]")
     B, T, Hqk, DK = q.shape
-    _, _, Hv, DV = v.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if g.dtype != torch.float32 or beta.dtype != torch.float32:
-        raise TypeError("g and beta must be float32")
-    if s0 is not None and (s0.dtype != torch.float32 or not s0.is_contiguous()):
-        raise TypeError("s0 must be a contiguous float32 tensor")
+    Hv, DV = v.shape[2], v.shape[3]
+    _dtype_code(q)  # fp16 or bf16
+    specs = [("q", q, (B, T, Hqk, DK), q.dtype), ("k", k, (B, T, Hqk, DK), q.dtype), ("v", v, (B, T, Hv, DV), q.dtype),
+             ("g", g, (B, T, Hv), torch.float32), ("beta", beta, (B, T, Hv), torch.float32)]
+    if s0 is not None:
+        specs.append(("s0", s0, (B, Hv, DK, DV), torch.float32))
+    if A is not None:
+        specs.append(("A", A, (B, T, Hv, 64), q.dtype))
+    _expect_all(specs)
     if scale is None:
         scale = 1.0 / math.sqrt(DK)
     if stream is None:
