@@ -11,6 +11,7 @@ Functions with the C ABI's names take raw device pointers and sizes:
     fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, M, N, D, scale, causal, dtype, stream)
     fa_fwd_strided(q_ptr, ..., D, q_strides, k_strides, v_strides, o_strides, scale, causal, dtype, stream)
     fa_fwd_splitkv(..., dtype, tiles_per_split, workspace_ptr, workspace_bytes, stream)
+    fa_fwd_splitkv_noalloc(..., dtype, tiles_per_split, stream)
     fa_fwd_splitkv_strided(..., D, q_strides, ..., o_strides, scale, ..., workspace_bytes, stream)
     fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles_per_split)
     fa_strerror(code), fa_tile_shape(B, Hq, M, D), fa_tile_counts(...), fa_schedule(...)
@@ -33,7 +34,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
 
 FA_F16, FA_BF16 = 0, 1
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, -1, -2, -3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_SCRATCH_TOO_SMALL = 0, -1, -2, -3, -4
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/fa.h: scratch of fa_fwd_splitkv_noalloc, per GPU
 
 _lib = None
 
@@ -74,6 +76,8 @@ def _load():
     lib.fa_splitkv_plan.restype = ci
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, ci, vp, sz, vp]
     lib.fa_fwd_splitkv.restype = ci
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, ci, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = ci
     sp = ctypes.POINTER(fa_strides)
     lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, sp, sp, sp, sp, cf, ci, ci, vp]
     lib.fa_fwd_strided.restype = ci
@@ -138,6 +142,14 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, causal, dtype, t
     """Raw C ABI call of the key-split forward (pointers as integers)."""
     return _load().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, M, N, D, float(scale), int(causal), int(dtype),
                                   int(tiles_per_split), workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, M, N, D, scale, causal, dtype, tiles_per_split,
+                           stream) -> int:
+    """Raw C ABI call of the key-split forward that allocates nothing (its partial results go to
+    the library's per-GPU scratch of FA_NOALLOC_SCRATCH_BYTES bytes)."""
+    return _load().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, M, N, D, float(scale), int(causal), int(dtype),
+                                          int(tiles_per_split), stream)
 
 
 def fa_splitkv_plan(B: int, Hq: int, Hkv: int, M: int, N: int, D: int, causal: bool, tiles_per_split: int = 0):
@@ -400,6 +412,6 @@ def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, s
 
 __all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_chunk_plan", "gdn_prefill",
            "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided",
-           "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_splitkv_plan", "fa_strides",
+           "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_splitkv_plan", "fa_strides",
            "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]

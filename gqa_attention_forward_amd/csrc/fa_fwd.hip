@@ -33,6 +33,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa.h"
@@ -830,6 +831,39 @@ static int split_plan(int B, int Hq, int Hkv, int M, int N, int D, bool causal, 
     return FA_OK;
 }
 
+// Scratch of the no-allocation key-split entry point: the partial results live in this
+// file-scope device array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address of each GPU's copy is looked up
+// once per device with hipGetSymbolAddress and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void *scratch_ptr[kMaxDevices];
+
+// Device address of the scratch of the current device, which must be the stream's device (it is
+// looked up on the first use on that device, with that device current).
+static int scratch_for_stream(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_LAUNCH;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_INVALID_ARG;
+        if ((int)sdev != dev) return FA_ERR_INVALID_ARG;  // another device's scratch would be the wrong memory
+    }
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_ERR_LAUNCH;
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return FA_OK;
+}
+
 template <typename T, int D>
 static hipError_t launch_split_d(const SplitParams &p, bool causal, hipStream_t stream)
 {
@@ -922,6 +956,8 @@ const char *fa_strerror(int code)
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128, pointers 16-byte aligned)";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH_TOO_SMALL:
+        return "the partial results need more than the no-allocation entry point's scratch (FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
     }
 }
@@ -1041,6 +1077,33 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
 {
     return fa_fwd_splitkv_strided(q, k, v, o, lse, B, Hq, Hkv, M, N, D, nullptr, nullptr, nullptr, nullptr, scale,
                                   causal, dtype, tiles_per_split, workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
+                           int M, int N, int D, float scale, int causal, int dtype, int tiles_per_split, void *stream)
+{
+    // every check that needs no device first, so that a bad call never touches the GPU
+    fa::SplitPlan pl;
+    int rc = fa::check_args(q, k, v, o, lse, B, Hq, Hkv, M, N, D, nullptr, nullptr, nullptr, nullptr, scale, dtype,
+                            &pl.sp);
+    if (rc != FA_OK) return rc;
+    rc = fa::split_plan(B, Hq, Hkv, M, N, D, causal != 0, tiles_per_split, &pl);
+    if (rc != FA_OK) return rc;
+    if (pl.sp.total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    if (pl.ws_bytes > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH_TOO_SMALL;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (pl.ws_bytes) {
+        if ((rc = fa::scratch_for_stream(s, &ws)) != FA_OK) return rc;
+        pl.sp.ws_lse = (float *)ws;
+        pl.sp.ws_o = (float *)((char *)ws + pl.ws_o_offset);
+    } else {
+        pl.sp.ws_lse = nullptr;
+        pl.sp.ws_o = nullptr;
+    }
+    hipError_t err = dtype == FA_F16 ? fa::launch_split<_Float16>(pl.sp, D, causal != 0, s)
+                                     : fa::launch_split<__bf16>(pl.sp, D, causal != 0, s);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -60,7 +60,8 @@ enum {
                                 unknown dtype, sizes whose element counts overflow int64 */
     FA_ERR_UNSUPPORTED = -2, /* D not in {64, 128}, a pointer or row not 16-byte aligned, a K/V row stride
                                 over 17 043 456 elements, or a grid beyond 2^31 - 1 workgroups */
-    FA_ERR_LAUNCH = -3       /* the kernel launch reported an error (hipGetLastError) */
+    FA_ERR_LAUNCH = -3,      /* the kernel launch reported an error (hipGetLastError) */
+    FA_ERR_SCRATCH_TOO_SMALL = -4 /* fa_fwd_splitkv_noalloc: the plan's partial results exceed its scratch */
 };
 
 /*
@@ -182,6 +183,28 @@ int fa_splitkv_plan(int B, int Hq, int Hkv, int M, int N, int D, int causal, int
 int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int M,
                    int N, int D, float scale, int causal, int dtype, int tiles_per_split, void *workspace,
                    size_t workspace_bytes, void *stream);
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * layouts, plan, kernels, results (bit for bit) and error codes as fa_fwd_splitkv, without the
+ * workspace: the partial results go to a scratch array of FA_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds in device memory, one per GPU, from the first call on that GPU until the process
+ * ends.  The call allocates nothing and frees nothing (no hipMalloc, no allocating library
+ * routine); the first call on a device looks up that device's scratch address.  The stream must
+ * belong to the current device (NULL: the current device's default stream); otherwise the call
+ * returns FA_ERR_INVALID_ARG without launching.
+ * Returns FA_ERR_SCRATCH_TOO_SMALL, before touching the GPU, when the plan's workspace (the size
+ * fa_splitkv_plan reports for the same arguments) exceeds FA_NOALLOC_SCRATCH_BYTES; plans that use
+ * no workspace never touch the scratch.
+ * All calls on one GPU share its scratch, which keeps the last call's contents (nothing in it needs
+ * to start at zero): two calls whose kernels may overlap on one GPU -- on different streams, or
+ * from different host threads without ordering -- race on it and give wrong results.  Calls on
+ * one stream are ordered and safe.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fa_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
+                           int M, int N, int D, float scale, int causal, int dtype, int tiles_per_split,
+                           void *stream);
 /* fa_fwd_splitkv on strided tensors (strides as for fa_fwd_strided; NULL = contiguous). */
 int fa_fwd_splitkv_strided(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
                            int M, int N, int D, const fa_strides *q_strides, const fa_strides *k_strides,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_texts():
     assert fa.fa_strerror(0) == "success"
-    for code in (-1, -2, -3, 12345):
+    for code in (-1, -2, -3, -4, 12345):
         assert isinstance(fa.fa_strerror(code), str) and fa.fa_strerror(code)
 
 
@@ -256,3 +256,25 @@ def test_headers_are_plain_c(tmp_path):
                    check=True)
     subprocess.run(["g++", "-std=c++11", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c++", "-I", inc,
                     str(src)], check=True)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(INCLUDE, "fa.h")).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch_before_touching_the_gpu():
+    """A plan whose partial results exceed the scratch is refused on the host (no GPU here: the
+    call must return before any HIP call)."""
+    args = (1, 64, 64, 4096, 8192, 128, 1)  # 64 heads x 32 query tiles, shares of 8 key tiles
+    _, _, ws = fa.fa_splitkv_plan(*args, 8)
+    assert ws > fa.FA_NOALLOC_SCRATCH_BYTES
+    B, Hq, Hkv, M, N, D, causal = args
+    rc = fa.fa_fwd_splitkv_noalloc(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, B, Hq, Hkv, M, N, D, 0.088, causal,
+                                   fa.FA_BF16, 8, None)
+    assert rc == fa.FA_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in fa.fa_strerror(rc)
+    # and the ordinary argument checks come first
+    assert fa.fa_fwd_splitkv_noalloc(None, 0x2000, 0x3000, 0x4000, 0x5000, B, Hq, Hkv, M, N, D, 0.088, causal,
+                                     fa.FA_BF16, 8, None) == fa.FA_ERR_INVALID_ARG
