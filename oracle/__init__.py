@@ -21,6 +21,8 @@ header states what is computed and which page passages each mode follows:
 * ``attn_probs``          -- the softmax weight matrix of one (b, h);
 * ``attn_bwd``            -- gradients of O with respect to q, k, v for an upstream dO,
   the chain rule of the definition written out (not on the pages; see the C file);
+* ``attn_bwd_slice``      -- the same gradients for one (b, kv head) group: dk and dv of a key
+  range and dq of chosen rows, parallel enough to check full-size problems;
 * ``gdn_chunked``, ``gdn_recurrent``, ``gdn_kkt`` -- the Gated DeltaNet chunked prefill of the
   page "lab3：GDN Prefill 前向优化" (section "算法与数据依赖"), the token recurrence it rewrites,
   and its A = (I + L)^-1 (``gdn_oracle.c``).
@@ -61,6 +63,9 @@ def _load():
         lib.oracle_set_threads.argtypes = [ci]
         lib.oracle_set_threads.restype = ci
         lib.oracle_attn_bwd.restype = ci
+        lib.oracle_attn_bwd_slice.argtypes = [u16p, u16p, u16p, u16p] + shape + [ci, ci, cl, cl, i64p, ctypes.c_int64,
+                                                                             dp, dp, dp]
+        lib.oracle_attn_bwd_slice.restype = ci
         gshape = [ci, ci, ci, ci, ci, ci, ci, cd]  # B, T, Hqk, Hv, DK, DV, C, scale
         lib.oracle_gdn_recurrent.argtypes = [u16p, u16p, u16p, ci, dp, dp, dp] + gshape + [dp, dp]
         lib.oracle_gdn_chunked.argtypes = [u16p, u16p, u16p, ci, dp, dp, dp, dp] + gshape + [dp, dp]
@@ -196,6 +201,28 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool, dtype: int | None = None):
                                  _ptr(dv, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dv
+
+
+def attn_bwd_slice(q, k, v, do, scale: float, causal: bool, b: int, hk: int, key_range, rows,
+                   dtype: int | None = None):
+    """Gradients for one (b, kv head) group only: (dq of `rows` [n, D], dk and dv of the keys
+    key_range = (j0, j1) [j1 - j0, D]) fp64; rows are indices (h - hk*g)*M + i of the group."""
+    dtype, (B, Hq, Hkv, M, N, D), qb, kb, vb = _common(q, k, v, dtype)
+    dob = _bits(do)
+    assert dob.shape == qb.shape
+    j0, j1 = (int(x) for x in key_range)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    dq = np.empty((rows.size, D), np.float64)
+    dk = np.empty((max(j1 - j0, 0), D), np.float64)
+    dv = np.empty((max(j1 - j0, 0), D), np.float64)
+    rc = _load().oracle_attn_bwd_slice(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                       _ptr(vb, ctypes.c_uint16), _ptr(dob, ctypes.c_uint16), dtype, B, Hq, Hkv, M,
+                                       N, D, float(scale), int(bool(causal)), int(b), int(hk), j0, j1,
+                                       _ptr(rows, ctypes.c_int64), rows.size, _ptr(dq, ctypes.c_double),
+                                       _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd_slice rejected its arguments")
     return dq, dk, dv
 
 

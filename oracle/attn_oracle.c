@@ -536,6 +536,172 @@ int oracle_attn_bwd(const uint16_t *q16, const uint16_t *k16, const uint16_t *v1
     return err ? -1 : 0;
 }
 
+/*
+ * The same gradients for a slice of one (batch b, KV head hk) group, organised so that each
+ * output has one owner and large problems can be checked: dk and dv of the keys j0 <= j < j1 of
+ * that KV head, and dq of a list of the group's query rows.  Same chain rule as oracle_attn_bwd:
+ *   pass 1, per query row i of each of the group's heads: m_i = max_j s_ij, l_i = sum_j
+ *     exp(s_ij - m_i), Delta_i = sum_j P_ij dP_ij with P_ij = exp(s_ij - m_i) / l_i and
+ *     dP_ij = dO_i . v_j (visible keys j);
+ *   pass 2, per key j of the slice: dv_j = sum_{h,i} P_ij dO_i and dk_j = scale sum_{h,i} dS_ij q_i
+ *     over the rows i that see j, dS_ij = P_ij (dP_ij - Delta_i);
+ *   pass 3, per listed row: dq_i = scale sum_j dS_ij k_j.
+ * rows: indices r = (h - hk g) M + i of the group's rows (g = Hq / Hkv); dq_rows [n_rows][D];
+ * dk_keys, dv_keys [j1 - j0][D].  Sums run in index order (rows, then heads, for pass 2).
+ */
+int oracle_attn_bwd_slice(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16, const uint16_t *do16,
+                          int dtype, int B, int Hq, int Hkv, int M, int N, int D, double scale, int causal, int b,
+                          int hk, long j0, long j1, const int64_t *rows, int64_t n_rows, double *dq_rows,
+                          double *dk_keys, double *dv_keys)
+{
+    if (!q16 || !k16 || !v16 || !do16 || B <= 0 || Hq <= 0 || Hkv <= 0 || M <= 0 || N <= 0 || D <= 0)
+        return -1;
+    if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1) || b < 0 || b >= B || hk < 0 || hk >= Hkv)
+        return -1;
+    if (j0 < 0 || j1 < j0 || j1 > N || (j1 > j0 && (!dk_keys || !dv_keys)) || n_rows < 0 ||
+        (n_rows > 0 && (!rows || !dq_rows)))
+        return -1;
+    const int g = Hq / Hkv;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= (int64_t)g * M)
+            return -1;
+    size_t nq = (size_t)B * Hq * M * D, nk = (size_t)B * Hkv * N * D;
+    problem p;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.M = M;
+    p.N = N;
+    p.D = D;
+    p.causal = causal;
+    p.scale = scale;
+    double *q = decode_all(q16, nq, dtype), *k = decode_all(k16, nk, dtype), *v = decode_all(v16, nk, dtype);
+    double *dO = decode_all(do16, nq, dtype);
+    double *mrow = (double *)malloc((size_t)g * M * sizeof(double));
+    double *lrow = (double *)malloc((size_t)g * M * sizeof(double));
+    double *drow = (double *)malloc((size_t)g * M * sizeof(double));
+    int err = 0;
+    if (!q || !k || !v || !dO || !mrow || !lrow || !drow) {
+        err = 1;
+        goto done;
+    }
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    /* pass 1: row statistics */
+#pragma omp parallel
+    {
+        double *z = (double *)malloc((size_t)N * sizeof(double));
+        if (!z) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 64)
+            for (long r = 0; r < (long)g * M; ++r) {
+                const int h = hk * g + (int)(r / M);
+                const long i = r % M;
+                const long nv = visible_count(&p, i);
+                if (nv == 0) {
+                    mrow[r] = -INFINITY;
+                    lrow[r] = 0.0;
+                    drow[r] = 0.0;
+                    continue;
+                }
+                const double *qi = q_row(&p, b, h, i);
+                const double *doi = dO + (((size_t)b * Hq + h) * M + i) * D;
+                double m = -INFINITY;
+                for (long j = 0; j < nv; ++j) {
+                    z[j] = score(&p, qi, k_row(&p, b, hk, j));
+                    if (z[j] > m)
+                        m = z[j];
+                }
+                double l = 0.0;
+                for (long j = 0; j < nv; ++j)
+                    l += exp(z[j] - m);
+                double delta = 0.0;
+                for (long j = 0; j < nv; ++j) {
+                    const double P = exp(z[j] - m) / l;
+                    const double *vj = v_row(&p, b, hk, j);
+                    double dp = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dp += doi[d] * vj[d];
+                    delta += P * dp;
+                }
+                mrow[r] = m;
+                lrow[r] = l;
+                drow[r] = delta;
+            }
+        }
+        free(z);
+    }
+    if (err)
+        goto done;
+    /* pass 2: dk, dv of the keys of the slice */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long j = j0; j < j1; ++j) {
+        double *dkj = dk_keys + (size_t)(j - j0) * D;
+        double *dvj = dv_keys + (size_t)(j - j0) * D;
+        for (int d = 0; d < D; ++d) {
+            dkj[d] = 0.0;
+            dvj[d] = 0.0;
+        }
+        const double *kj = k_row(&p, b, hk, j);
+        const double *vj = v_row(&p, b, hk, j);
+        for (int hh = 0; hh < g; ++hh) {
+            const int h = hk * g + hh;
+            for (long i = 0; i < M; ++i) {
+                if (j >= visible_count(&p, i))
+                    continue;
+                const long r = (long)hh * M + i;
+                const double *qi = q_row(&p, b, h, i);
+                const double *doi = dO + (((size_t)b * Hq + h) * M + i) * D;
+                const double P = exp(score(&p, qi, kj) - mrow[r]) / lrow[r];
+                double dp = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dp += doi[d] * vj[d];
+                const double dz = P * (dp - drow[r]);
+                for (int d = 0; d < D; ++d) {
+                    dkj[d] += scale * dz * qi[d];
+                    dvj[d] += P * doi[d];
+                }
+            }
+        }
+    }
+    /* pass 3: dq of the listed rows */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_rows; ++t) {
+        const long r = (long)rows[t];
+        const int h = hk * g + (int)(r / M);
+        const long i = r % M;
+        double *dqi = dq_rows + (size_t)t * D;
+        for (int d = 0; d < D; ++d)
+            dqi[d] = 0.0;
+        const long nv = visible_count(&p, i);
+        const double *qi = q_row(&p, b, h, i);
+        const double *doi = dO + (((size_t)b * Hq + h) * M + i) * D;
+        for (long j = 0; j < nv; ++j) {
+            const double *kj = k_row(&p, b, hk, j);
+            const double *vj = v_row(&p, b, hk, j);
+            const double P = exp(score(&p, qi, kj) - mrow[r]) / lrow[r];
+            double dp = 0.0;
+            for (int d = 0; d < D; ++d)
+                dp += doi[d] * vj[d];
+            const double dz = P * (dp - drow[r]);
+            for (int d = 0; d < D; ++d)
+                dqi[d] += scale * dz * kj[d];
+        }
+    }
+done:
+    free(q);
+    free(k);
+    free(v);
+    free(dO);
+    free(mrow);
+    free(lrow);
+    free(drow);
+    return err ? -1 : 0;
+}
+
 /* Threads for the OpenMP loops of later calls (n >= 1; n <= 0 leaves it unchanged).  Returns
  * the previous setting, so a caller can time a single-threaded run and restore it. */
 int oracle_set_threads(int n)

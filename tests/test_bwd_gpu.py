@@ -100,3 +100,31 @@ def test_bwd_key_gradients_sum_to_zero_on_gpu():
     mag = dk.float().abs().sum(dim=2).max().item()
     print(f"max |sum_j dk_j| = {s:.3e} vs sum |dk_j| = {mag:.3e}", flush=True)
     assert s <= 1e-2 * mag
+
+
+def test_long_causal_prefill_one_kv_head():
+    """The backward at the long causal GQA prefill's full size (1 x 32/8 heads x 16384^2, bf16,
+    peaky keys): dk and dv of one whole KV head (every key, summed over its 4 query heads) and dq
+    of sampled rows of those heads -- the first and last 64 of each head and 512 random ones --
+    against the oracle's per-group gradients."""
+    from gqa_attention_forward_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS["long_causal_gqa_16k"]
+    q, k, v, _ = make_inputs(w)
+    do = _dout(w.B, w.Hq, w.M, w.D, w.dtype, 1003)
+    dq_, dk_, dv_, ddo = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.attention_forward(dq_, dk_, dv_, causal=True, scale=w.scale, split_kv=False)
+    gq, gk, gv = fa.attention_backward(dq_, dk_, dv_, o, lse, ddo, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    hk, g = 3, w.Hq // w.Hkv
+    rng = np.random.default_rng(17)
+    rows = set()
+    for h in range(g):
+        rows.update(range(h * w.M, h * w.M + 64))
+        rows.update(range((h + 1) * w.M - 64, (h + 1) * w.M))
+    rows.update(rng.choice(g * w.M, 512, replace=False).tolist())
+    rows = np.array(sorted(rows), dtype=np.int64)
+    rq, rk, rv = oracle.attn_bwd_slice(q, k, v, do, w.scale, True, 0, hk, (0, w.N), rows)
+    got_q = gq[0, hk * g:(hk + 1) * g].reshape(g * w.M, w.D)[torch.from_numpy(rows).cuda()].cpu()
+    _check((got_q, gk[0, hk].cpu(), gv[0, hk].cpu()), (rq, rk, rv), w.dtype,
+           f"long causal prefill, KV head {hk}: all {w.N} keys, {rows.size} dq rows")

@@ -184,3 +184,45 @@ def test_zero_upstream_gradient():
     do = torch.zeros(1, 2, 6, 8, dtype=torch.float16)
     for g in oracle.attn_bwd(q, k, v, do, 0.3, True):
         assert np.all(g == 0.0)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_slice_matches_torch_autograd_float64(shape):
+    """The per-group slice mode (dk, dv of a key range; dq of chosen rows) against torch autograd,
+    for every group, a key range that starts and ends mid-sequence, and every row."""
+    B, Hq, Hkv, M, N, D, causal = shape
+    q, k, v = make_custom(B, Hq, Hkv, M, N, D, torch.bfloat16, seed=41)
+    do = _dout(B, Hq, M, D, torch.bfloat16, 42)
+    scale = 1.0 / math.sqrt(D)
+    tq, tk, tv, seen = _torch_grads(q, k, v, do, scale, causal)
+    g = Hq // Hkv
+    j0, j1 = N // 3, N - N // 4
+    for b in range(B):
+        for hk in range(Hkv):
+            rows = np.arange(g * M)
+            sq, sk, sv = oracle.attn_bwd_slice(q, k, v, do, scale, causal, b, hk, (j0, j1), rows)
+            ref_q = tq[b, hk * g:(hk + 1) * g].reshape(g * M, D)
+            row_seen = np.tile(seen, g)
+            np.testing.assert_allclose(sq[row_seen], ref_q[row_seen], rtol=1e-10, atol=1e-11)
+            assert np.all(sq[~row_seen] == 0.0)
+            np.testing.assert_allclose(sk, tk[b, hk, j0:j1], rtol=1e-10, atol=1e-11)
+            np.testing.assert_allclose(sv, tv[b, hk, j0:j1], rtol=1e-10, atol=1e-11)
+
+
+def test_slice_equals_whole_backward_and_rejects_bad_arguments():
+    B, Hq, Hkv, M, N, D = 2, 4, 2, 30, 41, 16
+    q, k, v = make_custom(B, Hq, Hkv, M, N, D, torch.float16, seed=43)
+    do = _dout(B, Hq, M, D, torch.float16, 44)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 0.25, True)
+    rows = np.array([0, 5, 29, 30, 59], dtype=np.int64)   # rows of both heads of the group
+    sq, sk, sv = oracle.attn_bwd_slice(q, k, v, do, 0.25, True, 1, 1, (0, N), rows)
+    ref_q = dq[1, 2:4].reshape(2 * M, D)[rows]
+    np.testing.assert_allclose(sq, ref_q, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sk, dk[1, 1], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sv, dv[1, 1], rtol=1e-12, atol=1e-14)
+    for bad in (dict(b=2), dict(hk=2), dict(key_range=(5, 3)), dict(key_range=(0, N + 1)),
+                dict(rows=np.array([2 * M], dtype=np.int64))):
+        a = dict(b=0, hk=0, key_range=(0, N), rows=rows)
+        a.update(bad)
+        with pytest.raises(ValueError):
+            oracle.attn_bwd_slice(q, k, v, do, 0.25, True, a["b"], a["hk"], a["key_range"], a["rows"])
