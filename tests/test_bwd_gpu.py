@@ -102,6 +102,7 @@ def test_bwd_key_gradients_sum_to_zero_on_gpu():
     assert s <= 1e-2 * mag
 
 
+@pytest.mark.timeout(400)  # the oracle's pass over one KV head at this size takes about a minute on 16 cores
 def test_long_causal_prefill_one_kv_head():
     """The backward at the long causal GQA prefill's full size (1 x 32/8 heads x 16384^2, bf16,
     peaky keys): dk and dv of one whole KV head (every key, summed over its 4 query heads) and dq
@@ -124,6 +125,7 @@ def test_long_causal_prefill_one_kv_head():
         rows.update(range((h + 1) * w.M - 64, (h + 1) * w.M))
     rows.update(rng.choice(g * w.M, 512, replace=False).tolist())
     rows = np.array(sorted(rows), dtype=np.int64)
+    print(f"GPU backward done; oracle over KV head {hk} ({g} query heads x {w.M} rows x {w.N} keys)", flush=True)
     rq, rk, rv = oracle.attn_bwd_slice(q, k, v, do, w.scale, True, 0, hk, (0, w.N), rows)
     got_q = gq[0, hk * g:(hk + 1) * g].reshape(g * w.M, w.D)[torch.from_numpy(rows).cuda()].cpu()
     _check((got_q, gk[0, hk].cpu(), gv[0, hk].cpu()), (rq, rk, rv), w.dtype,

@@ -153,3 +153,24 @@ def test_small_grid_workloads_auto(name):
     og = o.reshape(-1, w.D)[torch.from_numpy(rows)]
     lg = lse.reshape(-1)[torch.from_numpy(rows)]
     _check(og, lg, ro, rlse, w.dtype, what + f", {rows.size} sampled rows")
+
+
+def test_splitkv_many_split_tiles_merge_kernel():
+    """A plan with 18432 single-row query tiles, each split in two (36864 split work-groups and as
+    many merge rows): checked on sampled rows against the oracle, and every row against the
+    unsplit forward."""
+    B, Hq, Hkv, M, N, D = 64, 288, 288, 1, 128, 64
+    _, wgs, need = fa.fa_splitkv_plan(B, Hq, Hkv, M, N, D, True, 1)
+    assert wgs == 2 * B * Hq and need > 0
+    q, k, v = make_custom(B, Hq, Hkv, M, N, D, torch.bfloat16, seed=808)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o, lse = fa.attention_forward(dq, dk, dv, causal=True, split_kv=1)
+    op, lp = fa.attention_forward(dq, dk, dv, causal=True, split_kv=False)
+    torch.cuda.synchronize()
+    assert (o.float() - op.float()).abs().max().item() <= 2 * TOL[torch.bfloat16]
+    assert (lse - lp).abs().max().item() <= 1e-4
+    rows = np.random.default_rng(3).choice(B * Hq * M, 400, replace=False)
+    ro, rlse = oracle.attn_fwd_rows(q, k, v, 1.0 / math.sqrt(D), True, rows)
+    og = o.reshape(-1, D)[torch.from_numpy(rows).cuda()].cpu()
+    lg = lse.reshape(-1)[torch.from_numpy(rows).cuda()].cpu()
+    _check(og, lg, ro, rlse, torch.bfloat16, "merge-kernel plan, 400 sampled rows")
