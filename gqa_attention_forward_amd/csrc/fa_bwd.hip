@@ -56,7 +56,8 @@ struct Params {
     float *stats;  // [B*Hq][ceil(M/64)][128]
     int B, Hq, Hkv, M, N;
     int n_qt;           // query tiles of kRows per (b, h) (dQ) or key blocks of kRows per (b, kv head) (dK/dV)
-    long long total;    // workgroups
+    long long total;    // workgroups (< 2^31)
+    GridMap gm;         // workgroup id -> work, for this grid
     float c;            // scale * log2(e)
     float scale;
 };
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ql = lane & 31, hh = lane >> 5;
 
-    const TileCoord tc = logical_tile(xcd_remap(blockIdx.x, p.total), p.Hq, p.Hkv, p.n_qt, CAUSAL);
+    const TileCoord tc = logical_tile(xcd_remap(blockIdx.x, p.gm), p.gm, CAUSAL);
     const int g = p.Hq / p.Hkv, hk = tc.h / g;
     const int M = p.M, N = p.N;
     const int m0 = tc.qt * kRows;
@@ -290,10 +291,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
     const int kl = lane & 31, hh = lane >> 5;
 
     // (b, kv head) outer, key blocks inner (first blocks see the most queries when causal)
-    const long long L = xcd_remap(blockIdx.x, p.total);
-    const int kblk = (int)(L % p.n_qt);
-    const long long bhk = L / p.n_qt;
-    const int b = (int)(bhk / p.Hkv), hk = (int)(bhk % p.Hkv);
+    const GridPos gp = grid_pos(xcd_remap(blockIdx.x, p.gm), p.gm);  // p.gm divides by the key blocks
+    const int kblk = gp.inner;
+    const int b = gp.b, hk = gp.hk;
+    const long long bhk = (long long)b * p.Hkv + hk;
     const int g = p.Hq / p.Hkv;
     const int M = p.M, N = p.N;
     const int n0 = kblk * kRows;
@@ -454,6 +455,7 @@ static hipError_t launch_d(Params p, bool causal, hipStream_t s)
     Params pq = p;
     pq.n_qt = (p.M + kRows - 1) / kRows;
     pq.total = (long long)p.B * p.Hq * pq.n_qt;
+    pq.gm = make_grid_map((unsigned)pq.total, p.Hq / p.Hkv, pq.n_qt, p.Hkv);
     if (causal)
         hipLaunchKernelGGL((dq_kernel<T, D, true>), dim3((unsigned)pq.total), dim3(256), 0, s, pq);
     else
@@ -462,6 +464,7 @@ static hipError_t launch_d(Params p, bool causal, hipStream_t s)
     Params pk = p;
     pk.n_qt = (p.N + kRows - 1) / kRows;
     pk.total = (long long)p.B * p.Hkv * pk.n_qt;
+    pk.gm = make_grid_map((unsigned)pk.total, pk.n_qt, 1, p.Hkv);  // logical index: (b, kv head), key block
     if (causal)
         hipLaunchKernelGGL((dkdv_kernel<T, D, true>), dim3((unsigned)pk.total), dim3(256), 0, s, pk);
     else

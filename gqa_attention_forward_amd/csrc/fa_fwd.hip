@@ -85,7 +85,8 @@ struct Params {
     long long q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
     int B, Hq, Hkv, M, N;
     int n_qt;           // query tiles per (b, h)
-    long long total;    // workgroups in the grid
+    long long total;    // workgroups in the grid (< 2^31)
+    GridMap gm;         // workgroup id -> work, for this grid
     float c;            // scale * log2(e)
 };
 
@@ -171,19 +172,18 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     const int hh = lane >> 5;   // which half of each 32-key block this lane holds
 
     // ---- A1: which (b, h, query tile) this workgroup computes
-    const long long L = xcd_remap(blockIdx.x, p.total);
+    const unsigned L = xcd_remap(blockIdx.x, p.gm);
     TileCoord tc;  // tc.h: the (first) query head of the workgroup's unit
     int rank = 0, split = 0, n_split = 1;
     int R = p.M;           // rows of the unit
     long long unit = 0;    // unit index (key-split mode)
     if constexpr (SPLIT) {
-        // logical order: (b, kv head), then query-tile rank with its shares, then the group's units
+        // logical order: (b, kv head), then query-tile rank with its shares, then the group's
+        // units (p.gm divides by the units per KV group and by the workgroups per unit)
         const int g = p.Hq / p.Hkv;
-        const int gu = g / p.pack;  // units per KV group
-        const int hg = (int)(L % gu);
-        const long long rest = L / gu;
-        const int j = (int)(rest % p.wg_per_head);
-        const long long bhk = rest / p.wg_per_head;
+        const GridPos gp = grid_pos(L, p.gm);
+        const int hg = gp.inner;
+        const int j = gp.mid;
         int lo = 0, hi = p.n_qt;  // prefix[lo] <= j < prefix[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -192,13 +192,13 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         rank = lo;
         split = j - p.prefix[lo];
         n_split = p.prefix[lo + 1] - p.prefix[lo];
-        tc.b = (int)(bhk / p.Hkv);
-        tc.h = (int)(bhk % p.Hkv) * g + hg * p.pack;
+        tc.b = gp.b;
+        tc.h = gp.hk * g + hg * p.pack;
         tc.qt = CAUSAL ? p.n_qt - 1 - rank : rank;
-        unit = bhk * gu + hg;
+        unit = ((long long)gp.b * p.Hkv + gp.hk) * p.gm.inner.d + hg;
         R = p.pack * p.M;
     } else {
-        tc = logical_tile(L, p.Hq, p.Hkv, p.n_qt, CAUSAL);
+        tc = logical_tile(L, p.gm, CAUSAL);
     }
     const int g = p.Hq / p.Hkv;
     const int hk = tc.h / g;
@@ -824,6 +824,7 @@ static int split_plan(int B, int Hq, int Hkv, int M, int N, int D, bool causal, 
     sp.pack = pack;
     sp.slot_rows = slot_rows;
     sp.total = heads * sp.wg_per_head;
+    if (sp.total <= 0x7fffffffLL) sp.gm = make_grid_map((unsigned)sp.total, g / pack, sp.wg_per_head, Hkv);
     pl->tiles = tiles;
     const size_t rows = (size_t)heads * sp.slots * sp.slot_rows;
     pl->ws_o_offset = (rows * sizeof(float) + 255) & ~(size_t)255;
@@ -993,7 +994,9 @@ int fa_schedule(int B, int Hq, int Hkv, int M, int D, int causal, long long wg, 
     const int n_qt = (M + BM - 1) / BM;
     const long long total = (long long)B * Hq * n_qt;
     if (wg < 0 || wg >= total) return FA_ERR_INVALID_ARG;
-    fa::TileCoord c = fa::logical_tile(fa::xcd_remap(wg, total), Hq, Hkv, n_qt, causal != 0);
+    if (total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;  // the kernels' grid limit
+    const fa::GridMap gm = fa::make_grid_map((unsigned)total, Hq / Hkv, n_qt, Hkv);  // the kernel's mapping
+    fa::TileCoord c = fa::logical_tile(fa::xcd_remap((unsigned)wg, gm), gm, causal != 0);
     *b = c.b;
     *h = c.h;
     *q_tile = c.qt;
@@ -1014,6 +1017,7 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
     p.n_qt = (M + BM - 1) / BM;
     p.total = (long long)B * Hq * p.n_qt;
     if (p.total > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;  // one-dimensional grid limit
+    p.gm = fa::make_grid_map((unsigned)p.total, Hq / Hkv, p.n_qt, Hkv);
 
     hipStream_t s = (hipStream_t)stream;
     const fa::LaunchShape ls = fa::launch_shape(B, Hq, M, N, D);

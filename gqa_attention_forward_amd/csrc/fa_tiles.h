@@ -68,14 +68,78 @@ __host__ __device__ inline KvRange unit_kv_range(int m0, int BM, int BN, int M, 
     return kv_range_rows(0, M - 1, BN, M, N, causal);
 }
 
+// Division of an unsigned n < 2^31 by a divisor d >= 1 known at launch time, as a multiply-high,
+// an add and a shift: with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// floor(n / d) = (mulhi(n, m) + n) >> s (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", PLDI 1994, section 4; mulhi(n, m) <= n, so the sum fits 32 bits).  A
+// workgroup's tile coordinates then cost a handful of scalar instructions instead of the long
+// expansion of an integer division by a runtime value.
+struct FastDiv {
+    unsigned d, m, s;
+};
+
+inline FastDiv make_fastdiv(unsigned d)  // d >= 1
+{
+    unsigned s = 0;
+    while ((1ull << s) < d) ++s;
+    FastDiv f;
+    f.d = d;
+    f.m = (unsigned)((((1ull << s) - d) << 32) / d + 1);
+    f.s = s;
+    return f;
+}
+
+__host__ __device__ inline unsigned fdiv(unsigned n, const FastDiv &f)
+{
+    const unsigned t = (unsigned)(((unsigned long long)n * f.m) >> 32);
+    return (t + n) >> f.s;
+}
+
+// Everything a workgroup needs to find its work, computed once per launch on the host.  The grid
+// has total < 2^31 workgroups.  Logical index L = ((bhk * n_mid) + mid) * n_inner + inner, with
+// bhk = b * Hkv + kv head.
+struct GridMap {
+    unsigned xcd_q, xcd_rem;  // total / kNumXcd and total % kNumXcd
+    FastDiv inner;            // query heads of a KV group (per workgroup unit, in key-split mode)
+    FastDiv mid;              // query-tile ranks (workgroups per unit, in key-split mode)
+    FastDiv hkv;              // KV heads
+};
+
+inline GridMap make_grid_map(unsigned total, unsigned n_inner, unsigned n_mid, unsigned hkv)
+{
+    GridMap gm;
+    gm.xcd_q = total / kNumXcd;
+    gm.xcd_rem = total % kNumXcd;
+    gm.inner = make_fastdiv(n_inner);
+    gm.mid = make_fastdiv(n_mid);
+    gm.hkv = make_fastdiv(hkv);
+    return gm;
+}
+
 // Linear workgroup id -> logical work index, so that logical indices that are contiguous
 // run on one XCD: XCD x receives the logical block [start_x, start_x + count_x).
-__host__ __device__ inline long long xcd_remap(long long wg, long long total)
+static_assert((kNumXcd & (kNumXcd - 1)) == 0, "XCD count is a power of two");
+__host__ __device__ inline unsigned xcd_remap(unsigned wg, const GridMap &gm)
 {
-    long long xcd = wg % kNumXcd, slot = wg / kNumXcd;
-    long long q = total / kNumXcd, rem = total % kNumXcd;
-    long long start = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+    const unsigned xcd = wg % kNumXcd, slot = wg / kNumXcd;
+    const unsigned start = xcd < gm.xcd_rem ? xcd * (gm.xcd_q + 1) : gm.xcd_rem * (gm.xcd_q + 1) + (xcd - gm.xcd_rem) * gm.xcd_q;
     return start + slot;
+}
+
+// Logical index -> (inner, mid, b, kv head).
+struct GridPos {
+    int inner, mid, b, hk;
+};
+__host__ __device__ inline GridPos grid_pos(unsigned L, const GridMap &gm)
+{
+    GridPos g;
+    const unsigned rest = fdiv(L, gm.inner);
+    g.inner = (int)(L - rest * gm.inner.d);
+    const unsigned bhk = fdiv(rest, gm.mid);
+    g.mid = (int)(rest - bhk * gm.mid.d);
+    g.b = (int)fdiv(bhk, gm.hkv);
+    g.hk = (int)(bhk - (unsigned)g.b * gm.hkv.d);
+    return g;
 }
 
 struct TileCoord {
@@ -84,19 +148,15 @@ struct TileCoord {
 
 // Logical work index -> (b, h, query tile).  Logical order: (b, kv head) outermost, then the
 // query-tile rank (longest-first when causal), then the query heads of the KV group, so the
-// g heads that share one K/V stream and the same key range are adjacent.
-__host__ __device__ inline TileCoord logical_tile(long long L, int Hq, int Hkv, int n_qt, bool causal)
+// g heads that share one K/V stream and the same key range are adjacent.  gm.inner divides by
+// g = Hq / Hkv and gm.mid by the query tiles per head.
+__host__ __device__ inline TileCoord logical_tile(unsigned L, const GridMap &gm, bool causal)
 {
-    int g = Hq / Hkv;
-    int hg = (int)(L % g);
-    long long rest = L / g;
-    int rank = (int)(rest % n_qt);
-    long long bhk = rest / n_qt;
+    const GridPos gp = grid_pos(L, gm);
     TileCoord c;
-    c.b = (int)(bhk / Hkv);
-    int hk = (int)(bhk % Hkv);
-    c.h = hk * g + hg;
-    c.qt = causal ? n_qt - 1 - rank : rank;
+    c.b = gp.b;
+    c.h = gp.hk * (int)gm.inner.d + gp.inner;
+    c.qt = causal ? (int)gm.mid.d - 1 - gp.mid : gp.mid;
     return c;
 }
 

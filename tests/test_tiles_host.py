@@ -117,3 +117,40 @@ def test_accounting_visible_pairs_closed_forms():
     assert accounting.visible_pairs_per_head(512, 8192, True) == sum(min(8192, i + 1 + 7680) for i in range(512))
     assert accounting.visible_pairs_per_head(3, 1, True) == 1
     assert accounting.visible_pairs_per_head(7, 9, False) == 63
+
+
+def _exact_schedule(B, Hq, Hkv, n_qt, causal, wg):
+    """The schedule written with exact integer division: XCD x = wg % 8 owns the x-th block of
+    consecutive logical indices; logical order (b, kv head), query-tile rank, query head."""
+    total = B * Hq * n_qt
+    q, rem = divmod(total, 8)
+    xcd, slot = wg % 8, wg // 8
+    L = (xcd * (q + 1) if xcd < rem else rem * (q + 1) + (xcd - rem) * q) + slot
+    g = Hq // Hkv
+    rest, hg = divmod(L, g)
+    bhk, rank = divmod(rest, n_qt)
+    b, hk = divmod(bhk, Hkv)
+    return b, hk * g + hg, (n_qt - 1 - rank) if causal else rank
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,M,causal", [
+    (3, 21, 7, 1000, False),          # g = 3, 8 query tiles
+    (5, 15, 3, 777, True),            # g = 5
+    (7, 56, 8, 70000, True),          # g = 7, 274 query tiles
+    (64, 96, 32, 65536, False),       # 1.5 M workgroups
+    (8191, 32, 4, 8191 * 256, True),  # 2.147e9 workgroups, just under the 2^31 grid limit
+])
+def test_schedule_matches_exact_division(B, Hq, Hkv, M, causal):
+    """The kernels find their tile with multiply-high division by divisors fixed at launch; the
+    library's schedule (the same code) equals exact division on sampled and boundary workgroups."""
+    import numpy as np
+
+    BM, _ = fa.fa_tile_shape(B, Hq, M, 128)
+    n_qt = (M + BM - 1) // BM
+    total = B * Hq * n_qt
+    assert total < 2 ** 31
+    rng = np.random.default_rng(total % 1000)
+    wgs = set(range(min(total, 64))) | set(range(max(0, total - 64), total))
+    wgs |= set(int(x) for x in rng.integers(0, total, 3000))
+    for wg in sorted(wgs):
+        assert fa.fa_schedule(B, Hq, Hkv, M, 128, causal, wg) == _exact_schedule(B, Hq, Hkv, n_qt, causal, wg), wg
