@@ -154,6 +154,21 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     __shared__ __attribute__((aligned(16))) unsigned char sink_[1024];
     lds_u8 *smem = (lds_u8 *)smem_raw;
 
+    // Request every 64-byte line of the launch parameters at entry, behind one wait: left to
+    // itself the compiler loads each field where it is first used, behind its own wait, and each
+    // cold line of the argument segment then costs one more memory round trip before the first
+    // tile load is issued.  The parameters are the kernel's only argument (offset 0); later field
+    // loads hit the scalar cache.
+    {
+        typedef const __attribute__((address_space(4))) unsigned karg_u32;
+        karg_u32 *ka = (karg_u32 *)__builtin_amdgcn_kernarg_segment_ptr();
+        static_assert(sizeof(Params) <= 4 * 64 && sizeof(SplitParams) > 4 * 64, "argument lines touched below");
+        if constexpr (SPLIT)  // the fifth line holds the first share-table entries
+            asm volatile("" ::"s"(ka[0]), "s"(ka[16]), "s"(ka[32]), "s"(ka[48]), "s"(ka[64]));
+        else
+            asm volatile("" ::"s"(ka[0]), "s"(ka[16]), "s"(ka[32]), "s"(ka[48]));
+    }
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane((tid >> 6) / WG);  // key group
@@ -647,33 +662,70 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_split_kernel(SplitParams p)
 // normalised share output O_s, lse = log sum_s exp(lse_s) and O = sum_s exp(lse_s - lse) O_s.
 // A share that saw no key of a row has lse_s = -inf and weight 0; a row no share saw gets
 // O = 0 and lse = -inf.  D/4 lanes per row, 4 columns each.
+constexpr int kMergeRegShares = 16;  // shares a merge thread holds in registers
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_merge_kernel(SplitParams p)
 {
     constexpr int BM = 128, LPR = D / 4, RPB = 256 / LPR;
+    {  // every line of the launch parameters requested at once (as in the forward kernels)
+        typedef const __attribute__((address_space(4))) unsigned karg_u32;
+        karg_u32 *ka = (karg_u32 *)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" ::"s"(ka[0]), "s"(ka[16]), "s"(ka[32]), "s"(ka[48]), "s"(ka[64]));
+    }
     const int SR = p.slot_rows, units_per_b = p.Hq / p.pack;
-    const long long per_unit = (long long)p.n_split_ranks * SR;
+    // blockIdx.y is the query-tile rank, so the share table is read with scalar loads (a per-lane
+    // index would make it a vector load from the argument segment: one more memory round trip
+    // before any partial result can be addressed); blockIdx.x covers (unit, row of the slot)
+    const int rank = blockIdx.y;
     const long long r = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-    if (r >= (long long)p.B * units_per_b * per_unit) return;
+    if (r >= (long long)p.B * units_per_b * SR) return;
     const int col = (threadIdx.x % LPR) * 4;
-    const long long unit = r / per_unit;
-    const int rem = (int)(r % per_unit), rank = rem / SR, ri = rem % SR;
+    const long long unit = r / SR;
+    const int ri = (int)(r % SR);
     const int rl = (p.causal ? p.n_qt - 1 - rank : rank) * BM + ri;  // row of the unit
     if (rl >= p.pack * p.M) return;
     const int b = (int)(unit / units_per_b), h = (int)(unit % units_per_b) * p.pack + rl / p.M, i = rl % p.M;
     const int base = p.prefix[rank], ns = p.prefix[rank + 1] - base;
     const size_t s0 = ((size_t)unit * p.slots + base) * SR + ri;  // share s is slot s0 + s * SR
     float m = -INFINITY;
-    for (int s = 0; s < ns; ++s) m = fmaxf(m, p.ws_lse[s0 + (size_t)s * SR]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    if (m != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const size_t slot = s0 + (size_t)s * SR;
-            const float w = __expf(p.ws_lse[slot] - m);
-            wsum += w;
-            const f32x4 os = *(const f32x4 *)(p.ws_o + slot * D + col);
-            acc += w * os;
+    if (ns <= kMergeRegShares) {
+        // every partial lse and output row loaded at once (one memory round trip instead of two),
+        // then the same arithmetic in the same order as the general path below
+        float ls[kMergeRegShares];
+        f32x4 os[kMergeRegShares];
+#pragma unroll
+        for (int s = 0; s < kMergeRegShares; ++s) {
+            if (s < ns) {
+                const size_t slot = s0 + (size_t)s * SR;
+                ls[s] = p.ws_lse[slot];
+                os[s] = *(const f32x4 *)(p.ws_o + slot * D + col);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kMergeRegShares; ++s)
+            if (s < ns) m = fmaxf(m, ls[s]);
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int s = 0; s < kMergeRegShares; ++s) {
+                if (s < ns) {
+                    const float w = __expf(ls[s] - m);
+                    wsum += w;
+                    acc += w * os[s];
+                }
+            }
+        }
+    } else {
+        for (int s = 0; s < ns; ++s) m = fmaxf(m, p.ws_lse[s0 + (size_t)s * SR]);
+        if (m != -INFINITY) {
+            for (int s = 0; s < ns; ++s) {
+                const size_t slot = s0 + (size_t)s * SR;
+                const float w = __expf(p.ws_lse[slot] - m);
+                wsum += w;
+                const f32x4 os = *(const f32x4 *)(p.ws_o + slot * D + col);
+                acc += w * os;
+            }
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -824,6 +876,7 @@ static int split_plan(int B, int Hq, int Hkv, int M, int N, int D, bool causal, 
     sp.pack = pack;
     sp.slot_rows = slot_rows;
     sp.total = heads * sp.wg_per_head;
+    if (sp.slots && heads * slot_rows > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;  // the merge grid's x extent
     if (sp.total <= 0x7fffffffLL) sp.gm = make_grid_map((unsigned)sp.total, g / pack, sp.wg_per_head, Hkv);
     pl->tiles = tiles;
     const size_t rows = (size_t)heads * sp.slots * sp.slot_rows;
@@ -876,8 +929,9 @@ static hipError_t launch_split_d(const SplitParams &p, bool causal, hipStream_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.slots == 0) return e;
     constexpr int RPB = 256 / (D / 4);
-    const long long rows = (long long)p.B * (p.Hq / p.pack) * p.n_split_ranks * p.slot_rows;
-    hipLaunchKernelGGL((fa_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
+    const long long rows = (long long)p.B * (p.Hq / p.pack) * p.slot_rows;  // merge rows per split rank
+    hipLaunchKernelGGL((fa_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB), (unsigned)p.n_split_ranks),
+                       dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
