@@ -58,6 +58,10 @@ SHAPES = [
     (1, 12, 1, 100, 700, 64, True, torch.bfloat16, 2),      # tiles straddle head boundaries, causal
     (2, 8, 1, 33, 64, 128, True, torch.float16, 1),
     (1, 6, 2, 50, 40, 128, True, torch.bfloat16, 1),        # M > N: the first 10 rows of every head empty
+    # the merge holds up to 16 shares of a row in registers and loops over more
+    (1, 2, 1, 64, 1024, 64, False, torch.bfloat16, 1),      # 16 shares
+    (1, 2, 1, 64, 1088, 64, False, torch.float16, 1),       # 17 shares
+    (1, 4, 2, 200, 1500, 128, True, torch.float16, 1),      # up to 24 shares, two split query-tile ranks
     (1, 16, 2, 127, 3000, 128, False, torch.float16, 5),
     (16, 32, 8, 64, 512, 128, True, torch.float16, 0),      # automatic: stacked heads, no split
 ]
