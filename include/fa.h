@@ -165,7 +165,9 @@ const char *fa_strerror(int code);
  *   actually used (*tiles_used), the workgroup count of the split kernel (*workgroups) and the
  *   workspace size in bytes (*workspace_bytes; 0 when no query tile is split).  Returns FA_OK,
  *   FA_ERR_INVALID_ARG (null pointer, non-positive size, Hq % Hkv != 0) or FA_ERR_UNSUPPORTED
- *   (D not 64 or 128, more than 128 query tiles per head, i.e. M > 16384).
+ *   (D not 64 or 128, more than 128 query tiles per head, i.e. M > 16384, or split query tiles
+ *   whose merge would need more than 2^31 - 1 rows per query-tile rank, i.e. B * Hq * min(128, M)
+ *   beyond that when the query heads are not stacked).
  *
  * fa_fwd_splitkv: arguments, layouts, determinism and error codes as fa_fwd, plus
  *   tiles_per_split   as for fa_splitkv_plan (the plan is recomputed from the same arguments)
