@@ -126,6 +126,18 @@ def test_splitkv_auto_policy():
     assert used == 8 and wgs == 8 * 16
 
 
+def test_splitkv_plan_merge_grid_limit():
+    """The merge kernel's grid has one row of workgroups per split query-tile rank, covering
+    B * Hq * min(128, M) rows (heads not stacked): a plan beyond 2^31 - 1 such rows is refused,
+    one just below the limit is planned."""
+    per_b = 8 * 128  # Hq = Hkv = 8, M = 128: one 128-row tile per head, 4 key tiles, shares of 1
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_splitkv_plan(2 ** 31 // per_b + 1, 8, 8, 128, 256, 128, True, 1)
+    assert e.value.code == fa.FA_ERR_UNSUPPORTED
+    used, wgs, ws = fa.fa_splitkv_plan((2 ** 31 - 1) // per_b, 8, 8, 128, 256, 128, True, 1)
+    assert used == 1 and ws > 0
+
+
 SPLIT_GOOD = dict(GOOD, tiles=1, ws=0x100000, ws_bytes=1 << 30)
 
 
