@@ -31,6 +31,7 @@
 // banks: unit u of row r is stored at u ^ swz(r).  The tiles are copied HBM -> LDS by buffer
 // loads with LDS destination, each lane gathering the logical unit its LDS slot must hold.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 
@@ -245,16 +246,27 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
         // dS^T = P^T (dP^T - Delta); register r of block kb is key n0 + 32 kb + 8 (r/4) + 4 hh + r%4
         __builtin_amdgcn_s_setprio(0);
         const int n0 = t * kTile;
-        const bool masked = t >= kr.n_full;
+        // the element loop is compiled twice, with and without the mask, so that tiles every row
+        // sees entirely run no per-element mask code (a uniform test picks the copy; in the dK/dV
+        // kernel the second copy made the compiler spill, so that one keeps its uniform branches)
+        auto p_ds = [&](auto mask_c) {
+            constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2));
-                if (masked) pr = key < N && (!CAUSAL || key <= causal_lim) ? pr : 0.f;
-                s[kb][r] = pr * (dp[kb][r] - delta);
-            }
+                for (int r = 0; r < 16; ++r) {
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2));
+                    if constexpr (MASK) {
+                        const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        pr = key < N && (!CAUSAL || key <= causal_lim) ? pr : 0.f;
+                    }
+                    s[kb][r] = pr * (dp[kb][r] - delta);
+                }
+        };
+        if (t >= kr.n_full)
+            p_ds(std::true_type{});
+        else
+            p_ds(std::false_type{});
         // dQ^T += K^T dS^T
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
