@@ -246,27 +246,24 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
         // dS^T = P^T (dP^T - Delta); register r of block kb is key n0 + 32 kb + 8 (r/4) + 4 hh + r%4
         __builtin_amdgcn_s_setprio(0);
         const int n0 = t * kTile;
-        // the element loop is compiled twice, with and without the mask, so that tiles every row
-        // sees entirely run no per-element mask code (a uniform test picks the copy; in the dK/dV
-        // kernel the second copy made the compiler spill, so that one keeps its uniform branches)
-        auto p_ds = [&](auto mask_c) {
-            constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2));
+                s[kb][r] = pr * (dp[kb][r] - delta);
+            }
+        // masked tiles (diagonal band, ragged tail): dS of the keys the row does not see is zero.
+        // One uniform branch around the whole pass, so unmasked tiles run no per-element mask code.
+        if (t >= kr.n_full) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2));
-                    if constexpr (MASK) {
-                        const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        pr = key < N && (!CAUSAL || key <= causal_lim) ? pr : 0.f;
-                    }
-                    s[kb][r] = pr * (dp[kb][r] - delta);
+                    const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    s[kb][r] = key < N && (!CAUSAL || key <= causal_lim) ? s[kb][r] : 0.f;
                 }
-        };
-        if (t >= kr.n_full)
-            p_ds(std::true_type{});
-        else
-            p_ds(std::false_type{});
+        }
         // dQ^T += K^T dS^T
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -408,13 +405,21 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(Params p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * gq + e;
-                float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
-                if (masked) {
-                    const int i = i0 + qi + e;
-                    x = kvalid && i < M && (!CAUSAL || key <= i + (N - M)) ? x : 0.f;
-                }
+                const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
                 s[r] = x;
                 dp[r] = x * (dp[r] - d4[e]);
+            }
+        }
+        // masked tiles (diagonal band, ragged ends): P and dS of the pairs the lane's key does not
+        // see are zero.  One uniform branch around the whole pass, so unmasked tiles run no
+        // per-element mask code (a second copy of the loop above made the compiler spill).
+        if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool vis = kvalid && i < M && (!CAUSAL || key <= i + (N - M));
+                s[r] = vis ? s[r] : 0.f;
+                dp[r] = vis ? dp[r] : 0.f;
             }
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries.  MFMA m: k-step
