@@ -231,15 +231,18 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
                       (unsigned)(lane * Hv * 4));
         }
     };
-    // V of this wave's block: column dv0 + 32 cb + ql, rows 32 tb + 8 q + 4 hh + e
+    // V of this wave's block: column dv0 + 32 cb + ql, rows 32 tb + 8 q + 4 hh + e of chunk c, one
+    // element per register (low half).  The buffer range ends at the chunk's last token, so rows
+    // past the sequence read as zero with no branch; the whole offset is the per-lane one.
+    const long long v_rs = (long long)Hv * DV * sizeof(T);  // bytes from one token's row to the next
+    const unsigned v_lane = (unsigned)((32 * tb + 4 * hh) * v_rs + ql * (long long)sizeof(T));
     auto load_v = [&](int c, unsigned (&vr)[16]) {
-        const int t0 = c * C;
-        const unsigned short *vb = (const unsigned short *)p.v;
+        const int t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
+        const T *vbase = (const T *)p.v + (((size_t)b * T_ + t0) * Hv + h) * DV + dv0 + 32 * cb;
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, (n - 1) * v_rs + 32 * (long long)sizeof(T));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int t = t0 + 32 * tb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            vr[r] = t < T_ ? (unsigned)vb[(((size_t)b * T_ + t) * Hv + h) * DV + dv0 + 32 * cb + ql] : 0u;
-        }
+        for (int r = 0; r < 16; ++r)
+            vr[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, v_lane + (unsigned)((8 * (r >> 2) + (r & 3)) * v_rs), 0, 0);
     };
 
     // state: wave w owns state rows (key dims) 32 w .. 32 w + 31 for both 32-column blocks j;
@@ -623,6 +626,8 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     if (B <= 0 || T <= 0 || Hqk <= 0 || Hv <= 0 || DK <= 0 || DV <= 0 || Hv % Hqk != 0) return FA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !isfinite(scale) || (dtype != FA_F16 && dtype != FA_BF16)) return FA_ERR_INVALID_ARG;
     if (DK != fa::gdn::DK || DV % fa::gdn::DVB != 0) return FA_ERR_UNSUPPORTED;
+    // V is read with 32-bit offsets over one 64-token chunk of [B, T, Hv, DV] rows
+    if ((long long)Hv * DV * 2 * fa::gdn::C > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)A | (uintptr_t)o |
                          (uintptr_t)s_final | (uintptr_t)s0 | (uintptr_t)g | (uintptr_t)beta;
     if (al & 15u) return FA_ERR_UNSUPPORTED;
