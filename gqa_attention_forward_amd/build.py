@@ -21,6 +21,10 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 VALU ops stay off: the compiler's plain scalar float code is used instead
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the Gated DeltaNet state walk (one wave per SIMD, so
+    # more than 256 registers allowed) otherwise keeps its state and chunk products in AGPRs and
+    # copies them to VGPRs every chunk; the attention kernels compile to the same code either way
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
     "-I" + os.path.join(PKG, "csrc"),
 ]
