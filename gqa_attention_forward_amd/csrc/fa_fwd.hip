@@ -122,10 +122,10 @@ struct SplitParams : Params {
 // KG = 2 (small grids): the W waves form two key groups of W / 2 waves over the same BM =
 // 16 W rows; group k takes the query tile's key tiles k, k + 2, ... with buffers of its own,
 // both groups walk the same number of tiles (the second one's last tile, when the count is
-// odd, lies past the visible range and is masked out entirely), and the second group's
-// running max, partial sums and output accumulators are merged into the first group's
-// through LDS before the epilogue: half the sequential key loop per workgroup, and two waves
-// per SIMD instead of one.
+// odd, lies past the visible range and is masked out entirely), and the two groups' running
+// maxima, partial sums and output accumulators are merged through LDS before the epilogue,
+// each group merging and storing half of the output columns: half the sequential key loop per
+// workgroup, and two waves per SIMD instead of one.
 template <typename T, int D, bool CAUSAL, int W, bool SPLIT, int KG, typename P>
 __device__ __forceinline__ void fa_fwd_body(const P &p)
 {
@@ -568,35 +568,55 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     }
 
     if constexpr (KG == 2) {
-        // merge the second key group's state into the first's, lane by lane (both hold the same
-        // rows in the same layout): value v of lane (wave, lane) at float (v * 64 WG + 64 wave + lane)
+        // Merge of the two key groups' states, lane by lane (both groups hold the same rows in the
+        // same layout).  Group k keeps the output column blocks [k DB/2, (k+1) DB/2): it hands the
+        // other half of its O accumulators, its running max and its partial sum to the other group
+        // through LDS, and both groups form the merged state of their own half with the same
+        // arithmetic (R12's rescale-and-add, group 0's term as the product inside the FMA).  Each
+        // group then stores its half of every row.
         __attribute__((address_space(3))) float *xf = (__attribute__((address_space(3))) float *)smem;
-        constexpr int NV = DB * 16;
-        static_assert((NV + 2) * 64 * WG * 4 <= KG * GROUP_BYTES, "merge area inside the tile buffers");
+        constexpr int HB = DB / 2, NVH = HB * 16, REG = NVH + 2;  // floats per lane a group hands over
+        static_assert(2 * REG * 64 * WG * 4 <= KG * GROUP_BYTES, "merge area inside the tile buffers");
         const int slot = wave * 64 + lane;
+        __attribute__((address_space(3))) float *mine = xf + grp * REG * 64 * WG;
+        const __attribute__((address_space(3))) float *other = xf + (1 - grp) * REG * 64 * WG;
         wait_loads();         // no load into LDS still in flight (the look-ahead ones included)
         __syncthreads();      // and every wave is done with the tile buffers
-        if (grp == 1) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) xf[(db * 16 + r) * 64 * WG + slot] = oacc[db][r];
-            xf[NV * 64 * WG + slot] = m_run;
-            xf[(NV + 1) * 64 * WG + slot] = l_part;
-        }
-        __syncthreads();
         if (grp == 0) {
-            const float m1 = xf[NV * 64 * WG + slot], l1 = xf[(NV + 1) * 64 * WG + slot];
-            const float m = fmaxf(m_run, m1);
-            const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m) * c);
-            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c);
-            l_part = a0 * l_part + a1 * l1;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < HB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] = a0 * oacc[db][r] + a1 * xf[(db * 16 + r) * 64 * WG + slot];
-            m_run = m;
+                for (int r = 0; r < 16; ++r) mine[(db * 16 + r) * 64 * WG + slot] = oacc[HB + db][r];
+        } else {
+#pragma unroll
+            for (int db = 0; db < HB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mine[(db * 16 + r) * 64 * WG + slot] = oacc[db][r];
         }
+        mine[NVH * 64 * WG + slot] = m_run;
+        mine[(NVH + 1) * 64 * WG + slot] = l_part;
+        __syncthreads();
+        const float m_o = other[NVH * 64 * WG + slot], l_o = other[(NVH + 1) * 64 * WG + slot];
+        const float m0 = grp == 0 ? m_run : m_o, m1 = grp == 0 ? m_o : m_run;  // group 0's, group 1's
+        const float l0 = grp == 0 ? l_part : l_o, l1 = grp == 0 ? l_o : l_part;
+        const float m = fmaxf(m0, m1);
+        const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - m) * c);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * c);
+        l_part = __builtin_fmaf(a1, l1, a0 * l0);
+        if (grp == 0) {
+#pragma unroll
+            for (int db = 0; db < HB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    oacc[db][r] = __builtin_fmaf(a1, other[(db * 16 + r) * 64 * WG + slot], a0 * oacc[db][r]);
+        } else {
+#pragma unroll
+            for (int db = 0; db < HB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    oacc[HB + db][r] = __builtin_fmaf(a1, oacc[HB + db][r], a0 * other[(db * 16 + r) * 64 * WG + slot]);
+        }
+        m_run = m;
     }
 
     // ---- A8: epilogue -- normalise once, write O and the logsumexp
@@ -606,7 +626,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
                                                    __builtin_bit_cast(unsigned, l_part), false, false);
         l_tot = __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
     }
-    if (qvalid && grp == 0) {
+    if (qvalid) {  // with two key groups each stores its half of the row's columns
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float lse = l_tot > 0.f ? (m_run * c + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
         const size_t row = ((size_t)tc.b * p.Hq + qhead) * (size_t)M + qpos;
@@ -630,6 +650,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
             T *og = (T *)p.o + tc.b * p.o_sb + qhead * p.o_sh + qpos * p.o_ss;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
+                if (KG == 2 && (db < DB / 2) != (grp == 0)) continue;
                 u32x4 w0, w1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -640,7 +661,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
                 dst[0] = w0;
                 dst[1] = w1;
             }
-            if (hh == 0) p.lse[row] = lse;
+            if (hh == 0 && grp == 0) p.lse[row] = lse;
         }
     }
 }
