@@ -195,7 +195,6 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     if constexpr (SPLIT) {
         // logical order: (b, kv head), then query-tile rank with its shares, then the group's
         // units (p.gm divides by the units per KV group and by the workgroups per unit)
-        const int g = p.Hq / p.Hkv;
         const GridPos gp = grid_pos(L, p.gm);
         const int hg = gp.inner;
         const int j = gp.mid;
@@ -208,15 +207,15 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         split = j - p.prefix[lo];
         n_split = p.prefix[lo + 1] - p.prefix[lo];
         tc.b = gp.b;
-        tc.h = gp.hk * g + hg * p.pack;
+        tc.h = (gp.hk * (int)p.gm.inner.d + hg) * p.pack;  // g = inner.d * pack heads per KV head
+        tc.hk = gp.hk;
         tc.qt = CAUSAL ? p.n_qt - 1 - rank : rank;
         unit = ((long long)gp.b * p.Hkv + gp.hk) * p.gm.inner.d + hg;
         R = p.pack * p.M;
     } else {
         tc = logical_tile(L, p.gm, CAUSAL);
     }
-    const int g = p.Hq / p.Hkv;
-    const int hk = tc.h / g;
+    const int hk = tc.hk;
     const int m0 = tc.qt * kBM;
     const int M = p.M, N = p.N;
     const KvRange kr = SPLIT ? unit_kv_range(m0, kBM, kBN, M, N, R, CAUSAL) : kv_range(m0, kBM, kBN, M, N, CAUSAL);

@@ -144,6 +144,7 @@ __host__ __device__ inline GridPos grid_pos(unsigned L, const GridMap &gm)
 
 struct TileCoord {
     int b, h, qt;
+    int hk;  // KV head of query head h
 };
 
 // Logical work index -> (b, h, query tile).  Logical order: (b, kv head) outermost, then the
@@ -157,6 +158,7 @@ __host__ __device__ inline TileCoord logical_tile(unsigned L, const GridMap &gm,
     c.b = gp.b;
     c.h = gp.hk * (int)gm.inner.d + gp.inner;
     c.qt = causal ? (int)gm.mid.d - 1 - gp.mid : gp.mid;
+    c.hk = gp.hk;
     return c;
 }
 
