@@ -261,6 +261,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     constexpr unsigned kPad = 0x7fffff00u;  // an offset past the end of every tile resource
     lds_u8 *const sink = KG == 1 ? (lds_u8 *)sink_ : smem + KG * GROUP_BYTES;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    __builtin_assume(wave_u >= 0 && wave_u < kWaves);
     // key rows at or past kv_end read as zero: the end of the keys, or of this workgroup's share
     // (the pipeline's look-ahead loads run past it)
     const int kv_end = (t0 + n_tiles) * kBN < N ? (t0 + n_tiles) * kBN : N;
@@ -268,16 +269,18 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     unsigned k_src[KI], v_src[VI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-        const int u = (wave_u + kWaves * i) * 64 + lane;  // 16-byte unit of the K tile this lane fills
-        const int slot = u / (KP / 16), unit = u % (KP / 16);  // LDS slot and physical unit
-        const int key = (slot & ~31) | pi32(slot & 31);    // slot order pi inside each 32-key block
-        k_src[i] = unit < UNITS && u < K_INSTR * 64 ? (unsigned)(key * k_rs + (unit ^ Lds<D>::k_swz(slot)) * 16) : kPad;
+        // (unsigned arithmetic and the wave's range let the compiler fold the divisions into
+        // shifts and drop the bound test when every wave's blocks exist)
+        const unsigned u = (unsigned)(wave_u + kWaves * i) * 64u + (unsigned)lane;  // 16-byte unit of the K tile
+        const unsigned slot = u / (KP / 16), unit = u % (KP / 16);  // LDS slot and physical unit
+        const unsigned key = (slot & ~31u) | (unsigned)pi32((int)(slot & 31u));  // slot order pi in each 32-key block
+        k_src[i] = unit < UNITS && u < K_INSTR * 64 ? key * (unsigned)k_rs + (unit ^ (unsigned)Lds<D>::k_swz((int)slot)) * 16u : kPad;
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
-        const int u = (wave_u + kWaves * i) * 64 + lane;
-        const int row = u / (VP / 16), unit = u % (VP / 16);
-        v_src[i] = unit < UNITS && u < V_INSTR * 64 ? (unsigned)(row * v_rs + (unit ^ Lds<D>::v_swz(row)) * 16) : kPad;
+        const unsigned u = (unsigned)(wave_u + kWaves * i) * 64u + (unsigned)lane;
+        const unsigned row = u / (VP / 16), unit = u % (VP / 16);
+        v_src[i] = unit < UNITS && u < V_INSTR * 64 ? row * (unsigned)v_rs + (unit ^ (unsigned)Lds<D>::v_swz((int)row)) * 16u : kPad;
     }
     // buffer resource of key tile t: its rows up to kv_end, so a row past it (every byte of which
     // lies at or beyond (rows - 1) * row_bytes + D * sizeof(T)) reads as zero
