@@ -29,32 +29,44 @@ template <int D> __device__ __forceinline__ u32x4 read_row(const lds_u8 *tile, i
 // the 4 rows of column pi(l % 32), so the accumulator register r of half hh is column
 // 32 db + 16 hh + r.  Rows differ from the base by multiples of 16 (tt, 32-row blocks), which
 // leave swz unchanged, so the offsets depend on (db, lo/hi) only.
+template <int D> __device__ __forceinline__ unsigned tr_off(int lane, int db, int hi)
+{
+    const int hh = lane >> 5, G = (lane >> 4) & 1, s = lane & 15, e = s >> 2, j = s & 3;
+    const int row = 8 * hi + 4 * hh + e;
+    const int u = 4 * db + 2 * (j & 1) + G;
+    return (unsigned)(row * (2 * D) + ((u ^ swz<D>(row)) * 16) + 8 * (j >> 1));
+}
+
 template <int D> struct TrOffsets {
     static constexpr int DB = D / 32;
     unsigned off[DB][2];
     __device__ TrOffsets(int lane)
     {
-        const int hh = lane >> 5, G = (lane >> 4) & 1, s = lane & 15, e = s >> 2, j = s & 3;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int hi = 0; hi < 2; ++hi) {
-                const int row = 8 * hi + 4 * hh + e;
-                const int u = 4 * db + 2 * (j & 1) + G;
-                off[db][hi] = (unsigned)(row * (2 * D) + ((u ^ swz<D>(row)) * 16) + 8 * (j >> 1));
-            }
+            for (int hi = 0; hi < 2; ++hi) off[db][hi] = tr_off<D>(lane, db, hi);
     }
 };
 
-// X^T operand for k-step (row0 = 32-row block + 16 tt) and column block db
+// X^T operand for k-step row0 (32-row block + 16 tt), from the lane's two offsets of one column
+// block (tr_off with hi = 0 and 1)
 template <int D>
-__device__ __forceinline__ u32x4 read_tr(const lds_u8 *tile, const TrOffsets<D> &to, int row0, int db)
+__device__ __forceinline__ u32x4 read_tr_at(const lds_u8 *tile, int row0, unsigned off_lo, unsigned off_hi)
 {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + row0 * (2 * D) + to.off[db][0]));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + row0 * (2 * D) + to.off[db][1]));
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + row0 * (2 * D) + off_lo));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + row0 * (2 * D) + off_hi));
     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
     const u32x4 v = {lo2[0], lo2[1], hi2[0], hi2[1]};
     return v;
+}
+
+// X^T operand for k-step row0 and column block db (a compile-time index wherever the offsets
+// should stay in registers)
+template <int D>
+__device__ __forceinline__ u32x4 read_tr(const lds_u8 *tile, const TrOffsets<D> &to, int row0, int db)
+{
+    return read_tr_at<D>(tile, row0, to.off[db][0], to.off[db][1]);
 }
 
 }  // namespace fa

@@ -172,11 +172,12 @@ struct ChunkParams {
 template <typename T, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
 {
-    // LDS: two input buffers [Q | K | A | g | beta] and the per-chunk work arrays
+    // LDS: two input buffers [Q | K | A | g | beta | V] and the per-chunk work arrays
     constexpr int QK_TILE = C * DK * 2;        // swizzled, 256-byte rows
     constexpr int AP = 9 * 16;                 // A / work-array pitch in bytes (64 elements + pad)
     constexpr int A_TILE = C * AP;
-    constexpr int BUF = 2 * QK_TILE + A_TILE + 2 * 256;
+    constexpr int OFF_V = 2 * QK_TILE + A_TILE + 2 * 256;  // the chunk's V block, laid out as A
+    constexpr int BUF = OFF_V + A_TILE;
     constexpr int SP = 17 * 16;                // St pitch: 128 elements + pad
     constexpr int OFF_ST = 2 * BUF, OFF_WT = OFF_ST + DVB * SP, OFF_SC = OFF_WT + DVB * AP,
                   OFF_VN = OFF_SC + C * AP, OFF_VH = OFF_VN + DVB * AP, SMEM = OFF_VH + DVB * AP;
@@ -204,11 +205,15 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
     // the backward kernels): Q/K instruction j = wave + 4 i fills rows 4 j .. 4 j + 3
     const int qk_row = 4 * wave + (lane >> 4), qk_phys = lane & 15;
     const unsigned qk_src = (unsigned)(qk_row * qk_rs + ((qk_phys ^ swz<DK>(qk_row)) * 16));
-    unsigned a_src[3];
+    // V block of the chunk (its 64 tokens by this workgroup's 64 state columns): the same layout
+    // and copy pattern as A, a token's row being v_rs bytes after the previous one
+    const long long v_rs = (long long)Hv * DV * sizeof(T);
+    unsigned a_src[3], v_src[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {  // A instruction j = wave + 4 i (< 9) fills units 64 j .. 64 j + 63
         const int u = (wave + 4 * i) * 64 + lane, row = u / 9, unit = u % 9;
         a_src[i] = unit < 8 && row < C ? (unsigned)(row * a_rs + unit * 16) : 0x7fffff00u;
+        v_src[i] = unit < 8 && row < C ? (unsigned)(row * v_rs + unit * 16) : 0x7fffff00u;
     }
     auto issue = [&](int c, int buf) {
         const int t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
@@ -225,26 +230,18 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
 #pragma unroll
         for (int i = 0; i < 3; ++i)
             if (wave + 4 * i < 9) lds_load16(ra, (lds_void *)(dst + 2 * QK_TILE + (wave + 4 * i) * 1024), a_src[i]);
+        // tokens past the sequence read as zero (the range ends at the chunk's last token)
+        const __amdgpu_buffer_rsrc_t rv = rsrc((const T *)p.v + (((size_t)b * T_ + t0) * Hv + h) * DV + dv0,
+                                               (n - 1) * v_rs + DVB * (long long)sizeof(T));
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            if (wave + 4 * i < 9) lds_load16(rv, (lds_void *)(dst + OFF_V + (wave + 4 * i) * 1024), v_src[i]);
         if (wave < 2) {  // g (wave 0) and beta (wave 1): 64 floats, one per lane
             const float *src = (wave == 0 ? gbase : bbase) + (size_t)t0 * Hv;
             lds_load4(rsrc(src, (long long)(n - 1) * Hv * 4 + 4), (lds_void *)(dst + 2 * QK_TILE + A_TILE + wave * 256),
                       (unsigned)(lane * Hv * 4));
         }
     };
-    // V of this wave's block: column dv0 + 32 cb + ql, rows 32 tb + 8 q + 4 hh + e of chunk c, one
-    // element per register (low half).  The buffer range ends at the chunk's last token, so rows
-    // past the sequence read as zero with no branch; the whole offset is the per-lane one.
-    const long long v_rs = (long long)Hv * DV * sizeof(T);  // bytes from one token's row to the next
-    const unsigned v_lane = (unsigned)((32 * tb + 4 * hh) * v_rs + ql * (long long)sizeof(T));
-    auto load_v = [&](int c, unsigned (&vr)[16]) {
-        const int t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
-        const T *vbase = (const T *)p.v + (((size_t)b * T_ + t0) * Hv + h) * DV + dv0 + 32 * cb;
-        const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, (n - 1) * v_rs + 32 * (long long)sizeof(T));
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            vr[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, v_lane + (unsigned)((8 * (r >> 2) + (r & 3)) * v_rs), 0, 0);
-    };
-
     // state: wave w owns state rows (key dims) 32 w .. 32 w + 31 for both 32-column blocks j;
     // accumulator register r of half hh is row 32 w + 16 hh + r (the transposing read's order)
     f32x16 S[2];
@@ -296,26 +293,21 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         return *(const lds_u32x4 *)(arr + row * pitch + unit * 16);
     };
 
-    const TrOffsets<DK> tro(lane);
+    // transposing-read offsets of K for this wave's 32 key dims (column block `wave`)
+    const unsigned tr_lo = tr_off<DK>(lane, wave, 0), tr_hi = tr_off<DK>(lane, wave, 1);
     const float scale = p.scale;
-    // one element per register: packing pairs right after the loads would make the wave wait
-    // for them (and for the tile copies issued before them) before any of the chunk's work
-    unsigned vcur[16], vnext[16];
     issue(0, 0);
-    load_v(0, vcur);
     write_st();
     wait_vm0();
     __syncthreads();
 
     for (int c = 0; c < p.n_chunks; ++c) {
         const int buf = c & 1, t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
-        if (c + 1 < p.n_chunks) {
-            issue(c + 1, buf ^ 1);
-            load_v(c + 1, vnext);
-        }
+        if (c + 1 < p.n_chunks) issue(c + 1, buf ^ 1);
         if constexpr (SPLIT) store_st(c);
         const lds_u8 *qt = smem + buf * BUF, *kt = qt + QK_TILE, *at = kt + QK_TILE;
         const lds_f32 *gl = (const lds_f32 *)(at + A_TILE), *bl = gl + C;
+        const lds_u8 *vt = qt + OFF_V;
 
         // ---- U' = K S_c, Q S_c and K Q^T (this wave's blocks)
         // The output is computed transposed, O^T = S^T Q^T (+ V_new^T scores^T below), with the
@@ -352,7 +344,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * q + e;
                 const float eg = exp_(g4[e]);
-                const f32x2 vv = Elem<T>::unpack2(vcur[r]);
+                const f32x2 vv = Elem<T>::unpack2(
+                    *(const __attribute__((address_space(3))) unsigned short *)(vt + (r0 + e) * AP + (32 * cb + ql) * 2));
                 w[e] = b4[e] * (vv[0] - eg * U[r]);
                 // scores[t][s] for t = column, s = row: causal and gate-decayed
                 if constexpr (!SPLIT) s4[e] = r0 + e <= 32 * cb + ql ? KQ[r] * exp_(g_col - g4[e]) : 0.f;
@@ -419,7 +412,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             for (int sblk = 0; sblk < 2; ++sblk)
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const u32x4 a = read_tr<DK>(kt, tro, 32 * sblk + 16 * tt, wave);
+                    const u32x4 a = read_tr_at<DK>(kt, 32 * sblk + 16 * tt, tr_lo, tr_hi);
                     const u32x4 bv = *(const lds_u32x4 *)(vh + (32 * j + ql) * AP + (32 * sblk + 16 * tt + 8 * hh) * 2);
                     S[j] = Elem<T>::mfma(a, bv, S[j]);
                 }
@@ -428,8 +421,6 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         // phase, which every wave finished before the first barrier of this chunk, and the work
         // arrays written in the next chunk are read here only before the barrier that ends it.
         write_st();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) vcur[r] = vnext[r];
         wait_vm0();       // the next chunk's tiles (and this chunk's output stores) have landed
         __syncthreads();
     }
