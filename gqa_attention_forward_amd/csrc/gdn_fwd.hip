@@ -253,10 +253,6 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             S[j][r] = p.s0 ? p.s0[((size_t)bh * DK + d) * DV + e] : 0.f;
         }
     // bf16 copy of the state, transposed: St[column][key dim], 16 consecutive key dims per lane
-    // (two-kernel mode: the same 16-byte pieces are kept in `stash` and stored to the workspace
-    // as the chunk's starting state by store_st, once the chunk's loads have been issued, so
-    // that the wait for those loads at the end of the chunk does not also wait for the stores)
-    u32x4 stash[4];
     auto write_st = [&]() {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -269,17 +265,27 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
             lds_u8 *dst = st + (32 * j + ql) * SP + (32 * wave + 16 * hh) * 2;
             *(lds_u32x4 *)dst = w0;
             *(lds_u32x4 *)(dst + 16) = w1;
-            stash[2 * j] = w0;
-            stash[2 * j + 1] = w1;
         }
     };
+    // Two-kernel mode: the chunk's starting state and V_new go to the workspace from their LDS
+    // copies (St, and V_new staged in vn), each wave storing whole rows -- 16 bytes a lane, a
+    // column's 256 (St) or 128 (V_new) contiguous bytes per 16 or 8 lanes -- rather than the
+    // 16- and 8-byte pieces of many rows a lane holds in registers.  The state goes out at the
+    // top of the chunk, once the next chunk's loads have been issued.
     auto store_st = [&](int cidx) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            u32x4 *g = (u32x4 *)((T *)p.ws_st + (((size_t)bh * p.n_chunks + cidx) * DV + dv0 + 32 * j + ql) * DK +
-                                 32 * wave + 16 * hh);
-            g[0] = stash[2 * j];
-            g[1] = stash[2 * j + 1];
+        for (int i = 0; i < 4; ++i) {
+            const int col = 16 * wave + 4 * i + (lane >> 4), unit = lane & 15;
+            const u32x4 x = *(const lds_u32x4 *)(st + col * SP + unit * 16);
+            *(u32x4 *)((T *)p.ws_st + (((size_t)bh * p.n_chunks + cidx) * DV + dv0 + col) * DK + unit * 8) = x;
+        }
+    };
+    auto store_vn = [&](int cidx) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int col = 16 * wave + 8 * i + (lane >> 3), unit = lane & 7;
+            const u32x4 x = *(const lds_u32x4 *)(vn + col * AP + unit * 16);
+            *(u32x4 *)((T *)p.ws_vn + (((size_t)bh * p.n_chunks + cidx) * DV + dv0 + col) * C + unit * 8) = x;
         }
     };
     // 8-byte transposed write: 4 accumulator rows (registers 4 q .. 4 q + 3) of column `col`
@@ -367,14 +373,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         for (int q = 0; q < 4; ++q) {
             const int r0 = 32 * tb + 8 * q + 4 * hh;
             const f32x4 g4 = *(const lds_f32x4 *)(gl + r0);
-            if constexpr (SPLIT) {  // V_new^T rows (value columns) of 64 tokens
-                u32x2 w;
-                w[0] = Elem<T>::pack2(V[4 * q], V[4 * q + 1]);
-                w[1] = Elem<T>::pack2(V[4 * q + 2], V[4 * q + 3]);
-                *(u32x2 *)((T *)p.ws_vn + (((size_t)bh * p.n_chunks + c) * DV + dv0 + 32 * cb + ql) * C + r0) = w;
-            } else {
-                put4(vn, AP, 32 * cb + ql, r0, V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);
-            }
+            put4(vn, AP, 32 * cb + ql, r0, V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);  // V_new^T
             // decayed copy for the state update, positions with bits 2 and 3 of s swapped so that
             // the 8 rows one transposing K read pairs with are 16 contiguous bytes
             const int p0 = 32 * tb + 16 * (q >> 1) + 8 * hh + 4 * (q & 1);
@@ -383,6 +382,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         }
         __syncthreads();
 
+        if constexpr (SPLIT) store_vn(c);
         // ---- O = scale (exp(g) Q S_c + scores V_new)
         if constexpr (!SPLIT) {
 #pragma unroll
