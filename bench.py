@@ -59,8 +59,11 @@ def _parse():
                     help="time the forward, or the backward (dq, dk, dv from a forward's O and lse)")
     ap.add_argument("--layout", choices=["bhsd", "bshd"], default="bhsd",
                     help="memory layout of q, k, v, o: contiguous [B,H,S,D] or [B,S,H,D] buffers (strided path)")
-    ap.add_argument("--gdn-mode", choices=["auto", "one", "two"], default="auto",
-                    help="Gated DeltaNet workloads: the library's pick, the one-kernel or the two-kernel mode")
+    ap.add_argument("--gdn-mode", choices=["auto", "one", "two", "seg"], default="auto",
+                    help="Gated DeltaNet workloads: the library's pick, the one-kernel, the two-kernel or the "
+                         "segmented mode")
+    ap.add_argument("--gdn-segments", type=int, default=0,
+                    help="runs of chunks for --gdn-mode seg (0: the library's plan)")
     ap.add_argument("--split-kv", default="auto",
                     help="'auto' (key-split forward for small grids), 'off', or key tiles per share")
     return ap.parse_args()
@@ -248,14 +251,27 @@ def run_gdn(args, fa, w):
     sf = torch.empty((B, Hv, DK, DV), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     dt = 0 if q.dtype == torch.float16 else 1
-    ws_bytes = {"auto": lambda: fa.gdn_chunk_plan(B, T, Hv, DV), "one": lambda: 0,
-                "two": lambda: fa.gdn_chunk_workspace_size(B, T, Hv, DV)}[args.gdn_mode]()
+    segments = 1
+    if args.gdn_mode == "auto":
+        segments = fa.gdn_segment_plan(B, T, Hv, DV)
+    elif args.gdn_mode == "seg":
+        segments = args.gdn_segments or max(2, fa.gdn_segment_plan(B, T, Hv, DV))
+    if segments > 1:
+        ws_bytes = fa.gdn_segmented_workspace_size(B, T, Hv, DV, segments)
+    else:
+        ws_bytes = {"auto": lambda: fa.gdn_chunk_plan(B, T, Hv, DV), "one": lambda: 0,
+                    "two": lambda: fa.gdn_chunk_workspace_size(B, T, Hv, DV)}[args.gdn_mode]()
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def call():
-        rc = fa.gdn_chunk_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), A.data_ptr(),
-                              s0.data_ptr() if s0 is not None else None, o.data_ptr(), sf.data_ptr(), B, T, Hqk, Hv,
-                              DK, DV, w.scale, dt, ws.data_ptr() if ws_bytes else None, ws_bytes, stream.cuda_stream)
+        common = (q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), A.data_ptr(),
+                  s0.data_ptr() if s0 is not None else None, o.data_ptr(), sf.data_ptr(), B, T, Hqk, Hv, DK, DV,
+                  w.scale, dt)
+        if segments > 1:
+            rc = fa.gdn_chunk_fwd_segmented(*common, segments, ws.data_ptr() if ws_bytes else None, ws_bytes,
+                                            stream.cuda_stream)
+        else:
+            rc = fa.gdn_chunk_fwd(*common, ws.data_ptr() if ws_bytes else None, ws_bytes, stream.cuda_stream)
         assert rc == 0, rc
 
     for _ in range(args.warmup):
@@ -276,11 +292,14 @@ def run_gdn(args, fa, w):
     flops = accounting.gdn_flops(B, T, Hv, DK, DV)
     nbytes = accounting.gdn_bytes(B, T, Hqk, Hv, DK, DV, s0 is not None)
     assert torch.isfinite(sf).all().item(), "non-finite state"
-    path = "gdn_chunk_fwd (state walk + parallel outputs)" if ws_bytes else "gdn_chunk_fwd (one kernel)"
+    if segments > 1:
+        path = f"gdn_chunk_fwd_segmented ({segments} runs: transition walks, combine, output walks)"
+    else:
+        path = "gdn_chunk_fwd (state walk + parallel outputs)" if ws_bytes else "gdn_chunk_fwd (one kernel)"
     line = {"workload": w.name, "path": path, "ms": round(avg_ms, 4),
             "median_ms": round(durs[len(durs) // 2], 4), "tflops": round(flops / (avg_ms * 1e-3) / 1e12, 2),
             "compulsory_gbs": round(nbytes / (avg_ms * 1e-3) / 1e9, 1),
-            "workgroups": B * Hv * (DV // 64)}
+            "state_walkers": B * Hv * (DV // 64), "runs": segments}
     print(json.dumps(line), file=sys.stderr, flush=True)
     achieved = flops / (avg_ms * 1e-3) / 1e12
     return {

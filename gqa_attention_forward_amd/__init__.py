@@ -20,6 +20,8 @@ Functions with the C ABI's names take raw device pointers and sizes:
     gdn_kkt(k, g, beta, A, B, T, Hqk, Hv, DK, dtype, stream)
     gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, ws, ws_bytes, stream)
     gdn_chunk_workspace_size(B, T, Hv, DV), gdn_chunk_plan(B, T, Hv, DV)
+    gdn_chunk_fwd_segmented(q, k, ..., scale, dtype, segments, ws, ws_bytes, stream)
+    gdn_segmented_workspace_size(B, T, Hv, DV, segments), gdn_segment_plan(B, T, Hv, DV)
 
 ``attention_forward``, ``attention_backward`` and ``gdn_prefill`` are the torch-tensor
 convenience wrappers (torch is used only for device memory, workspaces and the current stream).
@@ -97,6 +99,13 @@ def _load():
     lib.gdn_chunk_workspace_size.restype = sz
     lib.gdn_chunk_plan.argtypes = [ci, ci, ci, ci, ctypes.POINTER(sz)]
     lib.gdn_chunk_plan.restype = ci
+    lib.gdn_chunk_fwd_segmented.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, ci, vp,
+                                            sz, vp]
+    lib.gdn_chunk_fwd_segmented.restype = ci
+    lib.gdn_segmented_workspace_size.argtypes = [ci, ci, ci, ci, ci]
+    lib.gdn_segmented_workspace_size.restype = sz
+    lib.gdn_segment_plan.argtypes = [ci, ci, ci, ci, ctypes.POINTER(ci)]
+    lib.gdn_segment_plan.restype = ci
     _lib = lib
     return lib
 
@@ -184,6 +193,28 @@ def gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, sc
     one-kernel mode; else the state walk plus the parallel output kernel)."""
     return _load().gdn_chunk_fwd(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, float(scale), int(dtype),
                                  workspace, int(workspace_bytes), stream)
+
+
+def gdn_chunk_fwd_segmented(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype, segments,
+                            workspace, workspace_bytes, stream) -> int:
+    """Raw C ABI call (include/gdn.h): the chunk recurrence with the chunks split into runs walked
+    in parallel (transition walks, start-state combine, output walks)."""
+    return _load().gdn_chunk_fwd_segmented(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, float(scale),
+                                           int(dtype), int(segments), workspace, int(workspace_bytes), stream)
+
+
+def gdn_segmented_workspace_size(B: int, T: int, Hv: int, DV: int, segments: int) -> int:
+    """Bytes of the gdn_chunk_fwd_segmented workspace (0 when the chunks form a single run)."""
+    return int(_load().gdn_segmented_workspace_size(B, T, Hv, DV, segments))
+
+
+def gdn_segment_plan(B: int, T: int, Hv: int, DV: int) -> int:
+    """Runs of chunks the library picks for the segmented mode (1: it picks a sequential mode)."""
+    n = ctypes.c_int()
+    rc = _load().gdn_segment_plan(B, T, Hv, DV, ctypes.byref(n))
+    if rc != FA_OK:
+        raise FaError(rc, "gdn_segment_plan")
+    return int(n.value)
 
 
 def gdn_chunk_workspace_size(B: int, T: int, Hv: int, DV: int) -> int:
@@ -361,13 +392,16 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     return dq, dk, dv
 
 
-def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, stream=None, two_kernel="auto"):
+def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, stream=None, two_kernel="auto",
+                segments: int | None = None):
     """Gated DeltaNet chunked prefill on contiguous device tensors: q, k [B,T,Hqk,128], v [B,T,Hv,DV]
     (fp16/bf16), g and beta [B,T,Hv] fp32 (g: cumulative log-gate inside each 64-token chunk),
     s0 [B,Hv,128,DV] fp32 or None.  A [B,T,Hv,64] (dtype) is computed with gdn_kkt when not given.
     two_kernel: True for the state walk plus the parallel output kernel (workspace from torch's
-    caching allocator), False for the one-kernel mode, "auto" for the library's pick
-    (gdn_chunk_plan); all give the same bits.
+    caching allocator), False for the one-kernel mode -- these two give the same bits -- and
+    "auto" for the library's pick: the segmented mode when gdn_segment_plan picks more than one
+    run, else gdn_chunk_plan's mode.  segments: an int >= 1 runs the segmented mode
+    (gdn_chunk_fwd_segmented) with that many runs of chunks (1 gives the one-kernel bits).
     Returns (o [B,T,Hv,DV], final state [B,Hv,128,DV] fp32, A)."""
     import torch
 
@@ -396,6 +430,19 @@ def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, s
     o = torch.empty((B, T, Hv, DV), dtype=q.dtype, device=q.device)
     sf = torch.empty((B, Hv, DK, DV), dtype=torch.float32, device=q.device)
     ws, ws_bytes = None, 0
+    if segments is None and two_kernel == "auto":
+        planned = gdn_segment_plan(B, T, Hv, DV)
+        segments = planned if planned > 1 else None
+    if segments is not None:
+        ws_bytes = gdn_segmented_workspace_size(B, T, Hv, DV, segments)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+        rc = gdn_chunk_fwd_segmented(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                                     A.data_ptr(), s0.data_ptr() if s0 is not None else None, o.data_ptr(),
+                                     sf.data_ptr(), B, T, Hqk, Hv, DK, DV, scale, dt, segments,
+                                     ws.data_ptr() if ws is not None else None, ws_bytes, stream)
+        if rc != FA_OK:
+            raise FaError(rc, "gdn_chunk_fwd_segmented")
+        return o, sf, A
     if two_kernel == "auto":
         ws_bytes = gdn_chunk_plan(B, T, Hv, DV)
     elif two_kernel:
@@ -411,6 +458,7 @@ def gdn_prefill(q, k, v, g, beta, s0=None, scale: float | None = None, A=None, s
 
 
 __all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_chunk_plan", "gdn_prefill",
+           "gdn_chunk_fwd_segmented", "gdn_segmented_workspace_size", "gdn_segment_plan",
            "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided",
            "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_splitkv_plan", "fa_strides",
            "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",

@@ -161,17 +161,30 @@ struct ChunkParams {
     // two-kernel mode: the state at each chunk start, [B*Hv][chunks][DV][DK] (dtype), and
     // V_new, [B*Hv][chunks][DV][64] (dtype), both transposed (state column / value column major)
     void *ws_st, *ws_vn;
-    int B, T, Hqk, Hv, DV, n_chunks, dv_blocks;
+    // segmented mode: the chunks form runs of seg_chunks (the last may be shorter), n_seg of them
+    // in the launch.  The transition walk's end state [M | Z] of each run but the last: ws_m
+    // holds M, [B*Hv][runs - 1][DK / 4][DK][4] fp32 (4-column groups, each column group's rows
+    // contiguous), ws_z holds Z, [B*Hv][runs - 1][DK][DV] fp32; ws_start the start state of each
+    // run but the first, [B*Hv][runs - 1][DK][DV] fp32.
+    float *ws_m, *ws_z, *ws_start;
+    int B, T, Hqk, Hv, DV, n_chunks, dv_blocks, n_seg, seg_chunks;
     float scale;
 };
 
-// SPLIT = false: the whole chunk step (state and output) in one kernel.  SPLIT = true: only
-// the sequential part -- U', W', V_new and the state update -- stores each chunk's starting
-// state and V_new (as the dtype operands the output products use) for out_kernel, which forms
-// the outputs of all chunks in parallel.
-template <typename T, bool SPLIT>
+// What a chunk walk computes.  WALK_FULL: state and outputs.  WALK_STATE: only the sequential
+// part -- U', W', V_new and the state update -- storing each chunk's starting state and V_new
+// for out_kernel.  WALK_TRANSITION: the state part over one run of chunks, with the state
+// widened to DK + DV columns: the first DK start as the identity and see zero values, the
+// others start at zero and see the run's values, so the end state is [M | Z] with M the run's
+// linear map of the state and Z its end state from zero (the recurrence is linear in the state
+// and each state column evolves on its own).
+constexpr int WALK_FULL = 0, WALK_STATE = 1, WALK_TRANSITION = 2;
+
+// One workgroup per (b, value head, run of chunks, 64 state columns) walks its run in order.
+template <typename T, int MODE>
 __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
 {
+    constexpr bool SPLIT = MODE != WALK_FULL;  // no Q tile, no outputs
     // LDS: two input buffers [Q | K | A | g | beta | V] and the per-chunk work arrays
     constexpr int QK_TILE = C * DK * 2;        // swizzled, 256-byte rows
     constexpr int AP = 9 * 16;                 // A / work-array pitch in bytes (64 elements + pad)
@@ -190,9 +203,14 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
     const int ql = lane & 31, hh = lane >> 5;
     const int tb = wave >> 1, cb = wave & 1;  // this wave's 32x32 output block of the chunk products
     const int dvblk = (int)(blockIdx.x % p.dv_blocks);
-    const long long bh = blockIdx.x / p.dv_blocks;
+    const long long rest = blockIdx.x / p.dv_blocks;
+    const int seg = (int)(rest % p.n_seg);
+    const long long bh = rest / p.n_seg;
     const int b = (int)(bh / p.Hv), h = (int)(bh % p.Hv), hk = h / (p.Hv / p.Hqk);
-    const int dv0 = dvblk * DVB;
+    // transition walk: column blocks below DK / DVB are the identity's columns (no values read)
+    const bool ident = MODE == WALK_TRANSITION && dvblk < DK / DVB;
+    const int dv0 = MODE == WALK_TRANSITION ? (ident ? 0 : dvblk * DVB - DK) : dvblk * DVB;
+    const int c_begin = seg * p.seg_chunks, c_end = min(p.n_chunks, c_begin + p.seg_chunks);
     const int T_ = p.T, Hv = p.Hv, DV = p.DV;
     const long long qk_rs = (long long)p.Hqk * DK * sizeof(T);  // row stride of q / k in bytes
     const long long a_rs = (long long)Hv * C * sizeof(T);
@@ -231,11 +249,13 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         for (int i = 0; i < 3; ++i)
             if (wave + 4 * i < 9) lds_load16(ra, (lds_void *)(dst + 2 * QK_TILE + (wave + 4 * i) * 1024), a_src[i]);
         // tokens past the sequence read as zero (the range ends at the chunk's last token)
-        const __amdgpu_buffer_rsrc_t rv = rsrc((const T *)p.v + (((size_t)b * T_ + t0) * Hv + h) * DV + dv0,
-                                               (n - 1) * v_rs + DVB * (long long)sizeof(T));
+        if (!ident) {
+            const __amdgpu_buffer_rsrc_t rv = rsrc((const T *)p.v + (((size_t)b * T_ + t0) * Hv + h) * DV + dv0,
+                                                   (n - 1) * v_rs + DVB * (long long)sizeof(T));
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
-            if (wave + 4 * i < 9) lds_load16(rv, (lds_void *)(dst + OFF_V + (wave + 4 * i) * 1024), v_src[i]);
+            for (int i = 0; i < 3; ++i)
+                if (wave + 4 * i < 9) lds_load16(rv, (lds_void *)(dst + OFF_V + (wave + 4 * i) * 1024), v_src[i]);
+        }
         if (wave < 2) {  // g (wave 0) and beta (wave 1): 64 floats, one per lane
             const float *src = (wave == 0 ? gbase : bbase) + (size_t)t0 * Hv;
             lds_load4(rsrc(src, (long long)(n - 1) * Hv * 4 + 4), (lds_void *)(dst + 2 * QK_TILE + A_TILE + wave * 256),
@@ -243,14 +263,21 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         }
     };
     // state: wave w owns state rows (key dims) 32 w .. 32 w + 31 for both 32-column blocks j;
-    // accumulator register r of half hh is row 32 w + 16 hh + r (the transposing read's order)
+    // accumulator register r of half hh is row 32 w + 16 hh + r (the transposing read's order).
+    // It starts as s0 (or zero) for the first run of chunks and as the combined start state for
+    // a later one; the transition walk starts from [I | 0].
+    const float *s_in = seg == 0 ? (p.s0 ? p.s0 + (size_t)bh * DK * DV : nullptr)
+                                 : p.ws_start + ((size_t)bh * (p.n_seg - 1) + seg - 1) * DK * DV;
     f32x16 S[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int d = 32 * wave + 16 * hh + r, e = dv0 + 32 * j + ql;
-            S[j][r] = p.s0 ? p.s0[((size_t)bh * DK + d) * DV + e] : 0.f;
+            if constexpr (MODE == WALK_TRANSITION)
+                S[j][r] = ident && d == dvblk * DVB + 32 * j + ql ? 1.f : 0.f;
+            else
+                S[j][r] = s_in ? s_in[(size_t)d * DV + e] : 0.f;
         }
     // bf16 copy of the state, transposed: St[column][key dim], 16 consecutive key dims per lane
     auto write_st = [&]() {
@@ -302,15 +329,15 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
     // transposing-read offsets of K for this wave's 32 key dims (column block `wave`)
     const unsigned tr_lo = tr_off<DK>(lane, wave, 0), tr_hi = tr_off<DK>(lane, wave, 1);
     const float scale = p.scale;
-    issue(0, 0);
+    issue(c_begin, 0);
     write_st();
     wait_vm0();
     __syncthreads();
 
-    for (int c = 0; c < p.n_chunks; ++c) {
-        const int buf = c & 1, t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
-        if (c + 1 < p.n_chunks) issue(c + 1, buf ^ 1);
-        if constexpr (SPLIT) store_st(c);
+    for (int c = c_begin; c < c_end; ++c) {
+        const int buf = (c - c_begin) & 1, t0 = c * C, n = T_ - t0 < C ? T_ - t0 : C;
+        if (c + 1 < c_end) issue(c + 1, buf ^ 1);
+        if constexpr (MODE == WALK_STATE) store_st(c);
         const lds_u8 *qt = smem + buf * BUF, *kt = qt + QK_TILE, *at = kt + QK_TILE;
         const lds_f32 *gl = (const lds_f32 *)(at + A_TILE), *bl = gl + C;
         const lds_u8 *vt = qt + OFF_V;
@@ -352,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
                 const float eg = exp_(g4[e]);
                 const f32x2 vv = Elem<T>::unpack2(
                     *(const __attribute__((address_space(3))) unsigned short *)(vt + (r0 + e) * AP + (32 * cb + ql) * 2));
-                w[e] = b4[e] * (vv[0] - eg * U[r]);
+                w[e] = b4[e] * ((ident ? 0.f : vv[0]) - eg * U[r]);
                 // scores[t][s] for t = column, s = row: causal and gate-decayed
                 if constexpr (!SPLIT) s4[e] = r0 + e <= 32 * cb + ql ? KQ[r] * exp_(g_col - g4[e]) : 0.f;
             }
@@ -373,7 +400,8 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         for (int q = 0; q < 4; ++q) {
             const int r0 = 32 * tb + 8 * q + 4 * hh;
             const f32x4 g4 = *(const lds_f32x4 *)(gl + r0);
-            put4(vn, AP, 32 * cb + ql, r0, V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);  // V_new^T
+            if constexpr (MODE != WALK_TRANSITION)  // V_new^T, for the outputs
+                put4(vn, AP, 32 * cb + ql, r0, V[4 * q], V[4 * q + 1], V[4 * q + 2], V[4 * q + 3]);
             // decayed copy for the state update, positions with bits 2 and 3 of s swapped so that
             // the 8 rows one transposing K read pairs with are 16 contiguous bytes
             const int p0 = 32 * tb + 16 * (q >> 1) + 8 * hh + 4 * (q & 1);
@@ -382,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         }
         __syncthreads();
 
-        if constexpr (SPLIT) store_vn(c);
+        if constexpr (MODE == WALK_STATE) store_vn(c);
         // ---- O = scale (exp(g) Q S_c + scores V_new)
         if constexpr (!SPLIT) {
 #pragma unroll
@@ -424,17 +452,107 @@ __global__ __launch_bounds__(256, 1) void chunk_kernel(ChunkParams p)
         wait_vm0();       // the next chunk's tiles (and this chunk's output stores) have landed
         __syncthreads();
     }
+    if constexpr (MODE == WALK_TRANSITION) {
+        if (ident) {
+            float *dst = p.ws_m + ((size_t)bh * p.n_seg + seg) * DK * DK;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = 32 * wave + 16 * hh + r, e = dv0 + 32 * j + ql;
-            p.s_final[((size_t)bh * DK + d) * DV + e] = S[j][r];
+                for (int r = 0; r < 16; ++r) {
+                    const int col = dvblk * DVB + 32 * j + ql;
+                    dst[((col >> 2) * DK + 32 * wave + 16 * hh + r) * 4 + (col & 3)] = S[j][r];
+                }
+        } else {
+            float *dst = p.ws_z + ((size_t)bh * p.n_seg + seg) * DK * DV;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    dst[(size_t)(32 * wave + 16 * hh + r) * DV + dv0 + 32 * j + ql] = S[j][r];
         }
+    } else if (seg == p.n_seg - 1) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int d = 32 * wave + 16 * hh + r, e = dv0 + 32 * j + ql;
+                p.s_final[((size_t)bh * DK + d) * DV + e] = S[j][r];
+            }
+    }
+}
+
+// Start states of the later runs of chunks in the segmented mode.  With run r's end state from
+// the transition walk, [M_r | Z_r],
+//     S_{r+1} = M_r S_r + Z_r,   S_0 = s0 (or zero),
+// in fp32: Z first, then the products over the key dim in ascending order.  One workgroup (8
+// waves) per (b, value head, 8 state columns); thread (d, quad) forms columns 2 quad and
+// 2 quad + 1 of state row d.  Only S is carried from run to run: M_{r+1} (64 KiB) is copied into
+// the other half of a double-buffered LDS area by buffer-to-LDS loads while run r's product
+// reads M_r, and lane l of a wave then reads row 32 w + l / 2's 4-column group, 512 contiguous
+// bytes a wave.
+struct CombineParams {
+    const float *m, *z, *s0;
+    float *start;
+    int n_runs;  // transition walks: the runs of chunks but the last
+    int DV;
+};
+
+__global__ __launch_bounds__(512) void combine_kernel(CombineParams p)
+{
+    __shared__ __attribute__((aligned(16))) float m_raw[2 * DK * DK];
+    __shared__ __attribute__((aligned(16))) float s_raw[DK * 8];
+    lds_f32 *Ml = (lds_f32 *)m_raw, *Sl = (lds_f32 *)s_raw;
+    typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int d = tid >> 2, e2 = 2 * (tid & 3);
+    const int DV = p.DV, eblocks = DV / 8;
+    const int e0 = (int)(blockIdx.x % eblocks) * 8 + e2;
+    const long long bh = blockIdx.x / eblocks;
+    auto issue = [&](int r, int buf) {  // instruction i = wave + 8 k copies bytes 1024 i .. 1024 i + 1023
+        const __amdgpu_buffer_rsrc_t rs = rsrc(p.m + ((size_t)bh * p.n_runs + r) * DK * DK, DK * DK * 4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = wave + 8 * k;
+            lds_load16(rs, (lds_void *)(Ml + buf * DK * DK + i * 256), (unsigned)(i * 1024 + 16 * lane));
+        }
+    };
+    auto load_z = [&](int r) { return *(const f32x2 *)(p.z + (((size_t)bh * p.n_runs + r) * DK + d) * DV + e0); };
+#pragma unroll
+    for (int i = 0; i < 2; ++i) Sl[d * 8 + e2 + i] = p.s0 ? p.s0[((size_t)bh * DK + d) * DV + e0 + i] : 0.f;
+    issue(0, 0);
+    f32x2 z = load_z(0);
+    wait_vm0();
+    __syncthreads();
+    for (int r = 0; r < p.n_runs; ++r) {
+        const int buf = r & 1;
+        f32x2 zn = {0.f, 0.f};
+        if (r + 1 < p.n_runs) {
+            issue(r + 1, buf ^ 1);
+            zn = load_z(r + 1);
+        }
+        const lds_f32 *mr = Ml + buf * DK * DK;
+        f32x2 acc = z;
+#pragma unroll
+        for (int j = 0; j < DK / 4; ++j) {
+            const f32x4 mv = *(const lds_f32x4 *)(mr + (j * DK + d) * 4);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x2 sv = *(const lds_f32x2 *)(Sl + (4 * j + jj) * 8 + e2);
+                acc[0] = __builtin_fmaf(mv[jj], sv[0], acc[0]);
+                acc[1] = __builtin_fmaf(mv[jj], sv[1], acc[1]);
+            }
+        }
+        __syncthreads();  // every thread has read this run's S and M
+        *(lds_f32x2 *)(Sl + d * 8 + e2) = acc;
+        *(f32x2 *)(p.start + (((size_t)bh * p.n_runs + r) * DK + d) * DV + e0) = acc;
+        wait_vm0();       // M_{r+1} and Z_{r+1} have landed
+        __syncthreads();
+        z = zn;
+    }
 }
 
 // Outputs of the two-kernel mode: one workgroup per (b, value head, chunk, 64 value columns),
-// all independent.  With the chunk's starting state S_c and V_new from chunk_kernel<T, true>,
+// all independent.  With the chunk's starting state S_c and V_new from chunk_kernel<T, WALK_STATE>,
 //     O = scale (exp(g) (Q S_c) + scores V_new)
 // by the same products, in the same order and on the same rounded operands as the fused
 // kernel (so both modes give identical bits): O^T = S_c^T Q^T, scaled by exp(g) per token,
@@ -609,9 +727,12 @@ int gdn_chunk_plan(int B, int T, int Hv, int DV, size_t *workspace_bytes)
     return FA_OK;
 }
 
-int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *A,
-                  const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv, int DK, int DV, float scale,
-                  int dtype, void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+// Argument checks shared by the chunk-recurrence entry points (before any HIP call).
+static int check_chunk_args(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const void *A, const float *s0, const void *o, const float *s_final, int B, int T, int Hqk,
+                            int Hv, int DK, int DV, float scale, int dtype)
 {
     if (!q || !k || !v || !g || !beta || !A || !o || !s_final) return FA_ERR_INVALID_ARG;
     if (B <= 0 || T <= 0 || Hqk <= 0 || Hv <= 0 || DK <= 0 || DV <= 0 || Hv % Hqk != 0) return FA_ERR_INVALID_ARG;
@@ -622,14 +743,17 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)A | (uintptr_t)o |
                          (uintptr_t)s_final | (uintptr_t)s0 | (uintptr_t)g | (uintptr_t)beta;
     if (al & 15u) return FA_ERR_UNSUPPORTED;
-    if (workspace) {
-        if (workspace_bytes < gdn_chunk_workspace_size(B, T, Hv, DV)) return FA_ERR_INVALID_ARG;
-        if ((uintptr_t)workspace & 255u) return FA_ERR_UNSUPPORTED;
-    }
     // tile copies use 32-bit offsets inside one chunk: 63 rows of q/k, A, g and beta
     if ((long long)Hqk * fa::gdn::DK * 2 * 64 > 0x7fff0000LL || (long long)Hv * 64 * 2 * 64 > 0x7fff0000LL)
         return FA_ERR_UNSUPPORTED;
-    fa::gdn::ChunkParams p;
+    return FA_OK;
+}
+
+static fa::gdn::ChunkParams chunk_params(const void *q, const void *k, const void *v, const float *g,
+                                         const float *beta, const void *A, const float *s0, void *o, float *s_final,
+                                         int B, int T, int Hqk, int Hv, int DV, float scale)
+{
+    fa::gdn::ChunkParams p = {};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -646,7 +770,34 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     p.DV = DV;
     p.n_chunks = (T + fa::gdn::C - 1) / fa::gdn::C;
     p.dv_blocks = DV / fa::gdn::DVB;
+    p.n_seg = 1;
+    p.seg_chunks = p.n_chunks;
     p.scale = scale;
+    return p;
+}
+
+template <int MODE>
+static void launch_walk(int dtype, long long grid, hipStream_t s, const fa::gdn::ChunkParams &p)
+{
+    if (dtype == FA_F16)
+        hipLaunchKernelGGL((fa::gdn::chunk_kernel<_Float16, MODE>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((fa::gdn::chunk_kernel<__bf16, MODE>), dim3((unsigned)grid), dim3(256), 0, s, p);
+}
+
+extern "C" {
+
+int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *A,
+                  const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv, int DK, int DV, float scale,
+                  int dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int rc = check_chunk_args(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype);
+    if (rc != FA_OK) return rc;
+    if (workspace) {
+        if (workspace_bytes < gdn_chunk_workspace_size(B, T, Hv, DV)) return FA_ERR_INVALID_ARG;
+        if ((uintptr_t)workspace & 255u) return FA_ERR_UNSUPPORTED;
+    }
+    fa::gdn::ChunkParams p = chunk_params(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DV, scale);
     p.ws_st = workspace;
     p.ws_vn = workspace ? (void *)((char *)workspace + ws_states_bytes(B, T, Hv, DV)) : nullptr;
     const long long grid = (long long)B * Hv * p.dv_blocks;
@@ -654,21 +805,135 @@ int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, c
     if (grid_out > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     if (!workspace) {
-        if (dtype == FA_F16)
-            hipLaunchKernelGGL((fa::gdn::chunk_kernel<_Float16, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((fa::gdn::chunk_kernel<__bf16, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+        launch_walk<fa::gdn::WALK_FULL>(dtype, grid, s, p);
         return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
     }
-    if (dtype == FA_F16)
-        hipLaunchKernelGGL((fa::gdn::chunk_kernel<_Float16, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((fa::gdn::chunk_kernel<__bf16, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    launch_walk<fa::gdn::WALK_STATE>(dtype, grid, s, p);
     if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
     if (dtype == FA_F16)
         hipLaunchKernelGGL((fa::gdn::out_kernel<_Float16>), dim3((unsigned)grid_out), dim3(256), 0, s, p);
     else
         hipLaunchKernelGGL((fa::gdn::out_kernel<__bf16>), dim3((unsigned)grid_out), dim3(256), 0, s, p);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Runs of chunks of the segmented mode for `segments` requested: runs of ceil(chunks / segments)
+// chunks (at most one per chunk), so that none is empty; returns their number.
+static int seg_runs(int T, int segments, int *seg_chunks)
+{
+    const int n_chunks = (T + fa::gdn::C - 1) / fa::gdn::C;
+    if (segments > n_chunks) segments = n_chunks;
+    const int len = (n_chunks + segments - 1) / segments;
+    *seg_chunks = len;
+    return (n_chunks + len - 1) / len;
+}
+
+// workspace of the segmented mode: M, then Z, then the start states (each 256-byte aligned),
+// per run but one
+static size_t seg_part_bytes(int B, int Hv, int cols, int runs)
+{
+    return ((size_t)B * Hv * (runs - 1) * fa::gdn::DK * cols * 4 + 255) & ~(size_t)255;
+}
+
+size_t gdn_segmented_workspace_size(int B, int T, int Hv, int DV, int segments)
+{
+    if (B <= 0 || T <= 0 || Hv <= 0 || DV <= 0 || segments <= 0) return 0;
+    int len;
+    const int runs = seg_runs(T, segments, &len);
+    if (runs == 1) return 0;
+    return seg_part_bytes(B, Hv, fa::gdn::DK, runs) + 2 * seg_part_bytes(B, Hv, DV, runs);
+}
+
+// Cost model of the chunk walks (µs, measured on MI355X over long and small-grid shapes): a
+// chunk step takes ~2.0 in the transition walk and ~3.0 in the output walk at one workgroup per
+// CU, 2.1 in the two-kernel state walk; the two-kernel output kernel ~5.3 per 512 (chunk,
+// 64-column) workgroups; a combine step ~3.5 (bound by fetching M_r); ~10 of launches.
+static double seg_cost(long long walkers, long long tr_walkers, int runs, int len)
+{
+    const double tr_rounds = (double)((tr_walkers * (runs - 1) + 255) / 256);
+    const double out_rounds = (double)((walkers * runs + 255) / 256);
+    return tr_rounds * len * 2.0 + out_rounds * len * 3.0 + (runs - 1) * 3.5 + 10.0;
+}
+
+static double seq_cost(long long walkers, int n_chunks)
+{
+    if (walkers <= 128) return n_chunks * 2.1 + (double)((walkers * n_chunks + 511) / 512) * 5.3 + 5.0;
+    return n_chunks * 3.0 * (double)((walkers + 255) / 256);
+}
+
+// The segmented mode walks runs of chunks in parallel at the price of a second (transition)
+// walk over every run but the last with DK + DV state columns; it pays when the sequential walk
+// leaves most CUs idle.  Picks the run count (at most 64) of least modelled time, and 1 (no
+// segmentation) unless that beats the sequential pick of gdn_chunk_plan by a fifth; only for
+// grids of at most 128 state walkers.
+int gdn_segment_plan(int B, int T, int Hv, int DV, int *segments)
+{
+    if (!segments) return FA_ERR_INVALID_ARG;
+    *segments = 1;
+    if (B <= 0 || T <= 0 || Hv <= 0 || DV <= 0) return FA_ERR_INVALID_ARG;
+    if (DV % fa::gdn::DVB != 0) return FA_ERR_UNSUPPORTED;
+    const long long walkers = (long long)B * Hv * (DV / fa::gdn::DVB);
+    const long long tr_walkers = (long long)B * Hv * ((fa::gdn::DK + DV) / fa::gdn::DVB);
+    const int n_chunks = (T + fa::gdn::C - 1) / fa::gdn::C;
+    if (walkers > 128 || n_chunks < 2) return FA_OK;
+    double best = 0.8 * seq_cost(walkers, n_chunks);
+    for (int want = 2; want <= 64 && want <= n_chunks; ++want) {
+        int len;
+        const int runs = seg_runs(T, want, &len);
+        if (runs != want) continue;  // the same runs as a smaller request
+        const double c = seg_cost(walkers, tr_walkers, runs, len);
+        if (c < best) {
+            best = c;
+            *segments = runs;
+        }
+    }
+    return FA_OK;
+}
+
+int gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const void *A, const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv,
+                            int DK, int DV, float scale, int dtype, int segments, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    const int rc = check_chunk_args(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DK, DV, scale, dtype);
+    if (rc != FA_OK) return rc;
+    if (segments <= 0) return FA_ERR_INVALID_ARG;
+    int len;
+    const int runs = seg_runs(T, segments, &len);
+    fa::gdn::ChunkParams p = chunk_params(q, k, v, g, beta, A, s0, o, s_final, B, T, Hqk, Hv, DV, scale);
+    hipStream_t s = (hipStream_t)stream;
+    if (runs == 1) {  // one run: the one-kernel mode
+        launch_walk<fa::gdn::WALK_FULL>(dtype, (long long)B * Hv * p.dv_blocks, s, p);
+        return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
+    if (!workspace || workspace_bytes < gdn_segmented_workspace_size(B, T, Hv, DV, segments)) return FA_ERR_INVALID_ARG;
+    if ((uintptr_t)workspace & 255u) return FA_ERR_UNSUPPORTED;
+    const long long bh = (long long)B * Hv;
+    const long long grid_tr = bh * (runs - 1) * ((fa::gdn::DK + DV) / fa::gdn::DVB);
+    const long long grid_out = bh * runs * p.dv_blocks;
+    if (grid_tr > 0x7fffffffLL || grid_out > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+    p.ws_m = (float *)workspace;
+    p.ws_z = (float *)((char *)workspace + seg_part_bytes(B, Hv, fa::gdn::DK, runs));
+    p.ws_start = (float *)((char *)p.ws_z + seg_part_bytes(B, Hv, DV, runs));
+    p.seg_chunks = len;
+    // transition walks of every run but the last
+    fa::gdn::ChunkParams pt = p;
+    pt.n_seg = runs - 1;
+    pt.dv_blocks = (fa::gdn::DK + DV) / fa::gdn::DVB;
+    launch_walk<fa::gdn::WALK_TRANSITION>(dtype, grid_tr, s, pt);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    fa::gdn::CombineParams pc;
+    pc.m = p.ws_m;
+    pc.z = p.ws_z;
+    pc.s0 = s0;
+    pc.start = p.ws_start;
+    pc.n_runs = runs - 1;
+    pc.DV = DV;
+    hipLaunchKernelGGL(fa::gdn::combine_kernel, dim3((unsigned)(bh * (DV / 8))), dim3(512), 0, s, pc);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    // every run again from its start state, forming the outputs; the last run writes s_final
+    p.n_seg = runs;
+    launch_walk<fa::gdn::WALK_FULL>(dtype, grid_out, s, p);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -105,6 +105,8 @@ class GdnWorkload:
     seed: int
     init_state: bool = False
     chunk: int = 64
+    gate_lo: float = 0.9     # per-token gate a ~ U(gate_lo, gate_lo + gate_span)
+    gate_span: float = 0.1
 
     @property
     def scale(self) -> float:
@@ -123,8 +125,9 @@ GDN_WORKLOADS = {
 def make_gdn_inputs(w: GdnWorkload, device: str | torch.device = "cpu", *, B=None, T=None):
     """Returns (q, k, v, g, beta, s0). Recipe, CPU generator seeded with w.seed, draw order:
     q, k, v ~ N(0, 1) in fp32; q and k rows scaled to unit L2 norm (the usual normalised
-    delta-rule keys), then rounded to the dtype; per (token, value head) a gate a ~ U(0.9, 1)
-    whose log is summed inside each chunk (g, fp32); beta ~ U(0, 1) (fp32); the initial state
+    delta-rule keys), then rounded to the dtype; per (token, value head) a gate
+    a ~ U(gate_lo, gate_lo + gate_span) (U(0.9, 1) by default) whose log is summed inside each
+    chunk (g, fp32); beta ~ U(0, 1) (fp32); the initial state
     ~ N(0, 0.1^2) (fp32) when the workload has one, else None.  B and T may be overridden for
     smaller parity cases with the same recipe."""
     B = w.B if B is None else B
@@ -136,7 +139,7 @@ def make_gdn_inputs(w: GdnWorkload, device: str | torch.device = "cpu", *, B=Non
     q = (q / q.norm(dim=-1, keepdim=True)).to(w.dtype)
     k = (k / k.norm(dim=-1, keepdim=True)).to(w.dtype)
     v = v.to(w.dtype)
-    a = 0.9 + 0.1 * torch.rand((B, T, w.Hv), generator=gen)
+    a = w.gate_lo + w.gate_span * torch.rand((B, T, w.Hv), generator=gen)
     la = torch.log(a)
     pad = (-T) % w.chunk
     la = torch.nn.functional.pad(la, (0, 0, 0, pad)).reshape(B, (T + pad) // w.chunk, w.chunk, w.Hv)

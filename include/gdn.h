@@ -42,13 +42,34 @@
  *     gdn_chunk_workspace_size(B, T, Hv, DV) bytes (`workspace_bytes` its size), and must not
  *     be in use by another call at the same time; its contents on entry do not matter.
  *   gdn_chunk_workspace_size returns that size (0 for a non-positive argument).
- * gdn_chunk_plan: the mode this library would pick for the shape: *workspace_bytes = the
- *   workspace size when the two-kernel mode is expected to be faster (its state walk then
+ * gdn_chunk_plan: the sequential mode this library would pick for the shape: *workspace_bytes =
+ *   the workspace size when the two-kernel mode is expected to be faster (its state walk then
  *   occupies at most half of the 256 CUs), else 0 (one kernel).  FA_ERR_INVALID_ARG for a null
  *   pointer or a non-positive size, FA_ERR_UNSUPPORTED for DV not a multiple of 64.
- * Both validate every argument before any HIP call (FA_ERR_INVALID_ARG: null pointer, bad size,
- * Hv % Hqk, scale not finite or <= 0, unknown dtype, a workspace smaller than needed;
- * FA_ERR_UNSUPPORTED: DK != 128, DV not a multiple of 64, misaligned pointer or workspace,
+ * gdn_chunk_fwd_segmented: the same recurrence with the chunks cut into runs that are walked in
+ *   parallel.  The recurrence is affine in the state, S_end = M S_start + Z for a run (M the run's
+ *   linear map of the state, Z its end state from zero), and each state column evolves on its own.
+ *   Three kernels on `stream`: (1) every run but the last is walked from [I | 0] with its values
+ *   seen only by the last DV columns, giving [M | Z] (fp32; the same operand rounding as the
+ *   sequential walk); (2) the runs' start states S_{r+1} = M_r S_r + Z_r, S_0 = s0, in fp32;
+ *   (3) every run is walked again from its start state as in the one-kernel mode, forming the
+ *   outputs, the last run writing s_final.  `segments` >= 1 asks for that many runs: runs of
+ *   ceil(chunks / segments) chunks (at most one run per chunk, none empty).  The result equals the
+ *   sequential modes' up to rounding (the products are re-associated), not bit for bit, and is
+ *   deterministic.  One run (segments == 1, or a one-chunk sequence) runs the one-kernel mode,
+ *   with its bits, and needs no workspace.  Otherwise `workspace` is caller-owned DEVICE memory,
+ *   256-byte aligned, at least gdn_segmented_workspace_size(B, T, Hv, DV, segments) bytes (M,
+ *   then Z, then the start states: 4 * 128 * (128 + 2 DV) bytes per (b, value head) and run but
+ *   one, each part rounded up to 256 bytes), not in use by another call at the same time; its
+ *   contents on entry do not matter.  FA_ERR_INVALID_ARG also for segments <= 0 or a missing or
+ *   too small workspace, FA_ERR_UNSUPPORTED for a misaligned one.
+ *   gdn_segmented_workspace_size returns that size (0 for one run or a non-positive argument).
+ * gdn_segment_plan: *segments = the run count this library would pick for the shape, or 1 when it
+ *   picks a sequential mode (gdn_chunk_plan) instead: only for grids of at most 128 state walkers
+ *   (B * Hv * DV / 64), from a cost model of the three kernels.  Errors as gdn_chunk_plan.
+ * gdn_kkt, gdn_chunk_fwd and gdn_chunk_fwd_segmented validate every argument before any HIP call
+ * (FA_ERR_INVALID_ARG: null pointer, bad size, Hv % Hqk, scale not finite or <= 0, unknown dtype,
+ * a workspace smaller than needed; FA_ERR_UNSUPPORTED: DK != 128, DV not a multiple of 64, misaligned pointer or workspace,
  * strides beyond 32-bit tile offsets, a grid beyond 2^31 - 1 workgroups), return FA_ERR_LAUNCH if
  * the launch fails, allocate nothing and do not synchronise.  Deterministic.
  */
@@ -68,6 +89,12 @@ int gdn_chunk_plan(int B, int T, int Hv, int DV, size_t *workspace_bytes);
 int gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta, const void *A,
                   const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv, int DK, int DV, float scale,
                   int dtype, void *workspace, size_t workspace_bytes, void *stream);
+size_t gdn_segmented_workspace_size(int B, int T, int Hv, int DV, int segments);
+int gdn_segment_plan(int B, int T, int Hv, int DV, int *segments);
+int gdn_chunk_fwd_segmented(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const void *A, const float *s0, void *o, float *s_final, int B, int T, int Hqk, int Hv,
+                            int DK, int DV, float scale, int dtype, int segments, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

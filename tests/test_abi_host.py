@@ -248,6 +248,70 @@ def test_gdn_chunk_plan():
         fa.gdn_chunk_plan(0, 64, 2, 128)
 
 
+def _gdn_seg(segments=8, **kw):
+    a = dict(GDN, T=1000)
+    a.update(kw)
+    return fa.gdn_chunk_fwd_segmented(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A"], a["s0"], a["o"], a["sf"],
+                                      a["B"], a["T"], a["Hqk"], a["Hv"], a["DK"], a["DV"], a["scale"], a["dtype"],
+                                      segments, a["ws"], a["ws_bytes"], None)
+
+
+def _seg_runs(T, segments):
+    chunks = (T + 63) // 64
+    length = -(-chunks // min(segments, chunks))
+    return -(-chunks // length), length
+
+
+@pytest.mark.parametrize("bad", [dict(q=None), dict(A=None), dict(sf=None), dict(T=0), dict(Hqk=2, Hv=3),
+                                 dict(scale=0.0), dict(dtype=5), dict(segments=0), dict(segments=-2)])
+def test_gdn_segmented_invalid(bad):
+    assert _gdn_seg(**bad) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(DK=64), dict(DV=96), dict(v=0x3008), dict(s0=0x9004)])
+def test_gdn_segmented_unsupported(bad):
+    assert _gdn_seg(**bad) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_gdn_segmented_workspace_size_and_check():
+    # runs of ceil(chunks / segments) chunks; per (b, value head) and run but the last: M (128 x 128),
+    # Z and a start state (128 x DV), fp32, each of the three parts' ends rounded up to 256 bytes
+    for B, T, Hv, DV, seg in [(1, 32768, 16, 128, 8), (2, 700, 3, 64, 5), (1, 200, 4, 128, 9), (1, 64, 2, 128, 4),
+                              (1, 1000, 4, 128, 1), (3, 1000, 1, 64, 6)]:
+        runs, _ = _seg_runs(T, seg)
+        part = lambda cols: -(-(B * Hv * (runs - 1) * 128 * cols * 4) // 256) * 256  # noqa: E731
+        want = 0 if runs == 1 else part(128) + 2 * part(DV)
+        assert fa.gdn_segmented_workspace_size(B, T, Hv, DV, seg) == want, (B, T, Hv, DV, seg)
+    for bad in [(0, 64, 2, 128, 2), (1, 0, 2, 128, 2), (1, 640, 2, 128, 0)]:
+        assert fa.gdn_segmented_workspace_size(*bad) == 0
+    need = fa.gdn_segmented_workspace_size(1, 1000, 2, 128, 8)
+    assert need > 0
+    assert _gdn_seg(ws=None, ws_bytes=0) == fa.FA_ERR_INVALID_ARG
+    assert _gdn_seg(ws=0x100000, ws_bytes=need - 1) == fa.FA_ERR_INVALID_ARG
+    assert _gdn_seg(ws=0x100080, ws_bytes=need) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_gdn_segment_plan():
+    # segmented only for grids of at most 128 state walkers (B * Hv * DV / 64) with two or more
+    # chunks, and only when the cost model gives it a clear gain
+    assert fa.gdn_segment_plan(1, 32768, 16, 128) > 1      # 32 walkers, 512 chunks
+    assert fa.gdn_segment_plan(1, 65536, 4, 64) > 1        # 4 walkers, 1024 chunks
+    assert fa.gdn_segment_plan(8, 4096, 32, 128) == 1      # 512 walkers
+    assert fa.gdn_segment_plan(1, 100, 129, 64) == 1       # 129 walkers
+    assert fa.gdn_segment_plan(1, 64, 2, 128) == 1         # one chunk
+    for shape in [(1, 32768, 16, 128), (1, 8192, 4, 128), (2, 8192, 16, 128), (1, 16384, 8, 128),
+                  (1, 65536, 4, 64), (4, 4096, 8, 128), (1, 3000, 1, 64)]:
+        runs = fa.gdn_segment_plan(*shape)
+        assert 1 <= runs <= 64
+        if runs > 1:  # a run count the segmented mode really forms, with a workspace
+            assert _seg_runs(shape[1], runs)[0] == runs
+            assert fa.gdn_segmented_workspace_size(*shape, runs) > 0
+    with pytest.raises(fa.FaError):
+        fa.gdn_segment_plan(1, 64, 2, 96)
+    with pytest.raises(fa.FaError):
+        fa.gdn_segment_plan(0, 64, 2, 128)
+
+
 def test_gdn_kkt_invalid():
     assert fa.gdn_kkt(None, 0x4000, 0x5000, 0x6000, 1, 64, 1, 2, 128, 1, None) == fa.FA_ERR_INVALID_ARG
     assert fa.gdn_kkt(0x2000, 0x4000, 0x5000, 0x6000, 1, 64, 1, 2, 64, 1, None) == fa.FA_ERR_UNSUPPORTED

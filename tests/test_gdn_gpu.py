@@ -5,6 +5,10 @@ gdn_kkt: A against the oracle's (I + L)^-1, within the rounding of A to the inpu
 gdn_chunk_fwd: output and final state against the oracle's chunk recurrence fed the same A (the
 GPU's, decoded), within the page's 5e-3 max error scaled by the reference's magnitude (floor 1);
 and against the token-by-token recurrence (exact A) within twice that.
+gdn_chunk_fwd_segmented: the same bars.  It re-associates the recurrence (run start states from
+the runs' linear maps), so it is compared with the oracle, not bit for bit with the sequential
+modes; gates close to 1 keep those maps far from zero, so the combine of start states is
+exercised (with the default gates a map dies out within a few chunks).
 """
 import math
 
@@ -112,12 +116,17 @@ def test_gdn_workload_full(name):
     o, sf, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale)
     torch.cuda.synchronize()
     assert torch.isfinite(sf).all() and torch.isfinite(o.float()).all()
-    for mode in (False, True):  # the library's pick equals both modes, bit for bit
-        o1, s1, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, two_kernel=mode)
-        torch.cuda.synchronize()
-        assert torch.equal(o, o1) and torch.equal(sf, s1), f"two_kernel={mode} differs"
-        del o1, s1
-    del dev
+    runs = fa.gdn_segment_plan(w.B, w.T, w.Hv, w.DV)
+    print(f"{name}: the library picks {runs} run(s) of chunks", flush=True)
+    # the sequential modes agree bit for bit; the library's pick is their result or, segmented,
+    # the explicit segmented call's
+    o_one, s_one, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, two_kernel=False)
+    o_two, s_two, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, two_kernel=True)
+    o_pick, s_pick, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, segments=runs)
+    torch.cuda.synchronize()
+    assert torch.equal(o_one, o_two) and torch.equal(s_one, s_two), "the two sequential modes differ"
+    assert torch.equal(o, o_pick) and torch.equal(sf, s_pick), "the library's pick differs from its mode"
+    del o_two, s_two, o_pick, s_pick, dev
     T = w.T
     sl = lambda t: t[:1].contiguous() if t is not None else None  # noqa: E731
     qb, kb, vb, gb, bb, s0b = (sl(t) for t in (q, k, v, g, beta, s0))
@@ -133,6 +142,58 @@ def test_gdn_workload_full(name):
     ro, rs = oracle.gdn_chunked(qb, kb, vb, gb, bb, A_gpu, w.scale, s0b)
     assert _err(og, ro, f"{name} O, all {T} tokens of batch 0, oracle on the GPU's A") <= TOL
     assert _err(sg, rs, f"{name} state after {(T + 63) // 64} chunks, oracle on the GPU's A") <= TOL
+    if runs > 1:  # the sequential result too
+        assert _err(o_one[:1].cpu().double().numpy(), ro, f"{name} O, one-kernel mode, oracle on the GPU's A") <= TOL
+        assert _err(s_one[:1].cpu().double().numpy(), rs, f"{name} state, one-kernel mode, oracle on the GPU's A") <= TOL
+    del o_one, s_one
     ro, rs = oracle.gdn_chunked(qb, kb, vb, gb, bb, A_ref, w.scale, s0b)
     assert _err(og, ro, f"{name} O, all {T} tokens of batch 0, oracle on its own A") <= 2 * TOL
     assert _err(sg, rs, f"{name} state after {(T + 63) // 64} chunks, oracle on its own A") <= 2 * TOL
+
+
+# B, T, Hqk, Hv, DV, dtype, init_state, (gate_lo, gate_span), run counts asked for
+SEG_CASES = [
+    (1, 1000, 2, 4, 128, torch.bfloat16, True, (0.999, 0.001), [2, 3, 16]),   # 16 chunks, one per run
+    (1, 200, 2, 4, 128, torch.bfloat16, True, (0.9, 0.1), [2, 4, 9]),         # ragged last chunk; 9 > chunks
+    (2, 700, 1, 3, 64, torch.float16, False, (0.99, 0.01), [3, 5]),           # runs of 4 and 3 chunks
+    (1, 64 * 40 + 17, 4, 4, 128, torch.bfloat16, True, (1.0, 0.0), [7, 41]),  # no decay at all
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "x".join(str(x) for x in c[:5]) +
+                         str(c[5]).split(".")[-1] + f"-s0{int(c[6])}-a{c[7][0]}")
+def test_gdn_segmented_matches_oracle(case):
+    B, T, Hqk, Hv, DV, dtype, init, (lo, span), runs = case
+    w = GdnWorkload("seg", B, T, Hqk, Hv, 128, DV, dtype, T + Hv, init_state=init, gate_lo=lo, gate_span=span)
+    q, k, v, g, beta, s0 = make_gdn_inputs(w)
+    dev = [t.cuda() if t is not None else None for t in (q, k, v, g, beta, s0)]
+    o1, s1, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, two_kernel=False)
+    torch.cuda.synchronize()
+    A_np = A.cpu().double().numpy() * _valid_cols(T)[None, :, None, :]
+    ro, rs = oracle.gdn_chunked(q, k, v, g, beta, A_np, w.scale, s0)
+    to, ts = oracle.gdn_recurrent(q, k, v, g, beta, w.scale, s0)
+    for P in runs:
+        o, sf, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, segments=P)
+        o2, s2, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, segments=P)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(sf, s2), "not deterministic"
+        assert torch.isfinite(o.float()).all() and torch.isfinite(sf).all()
+        og, sg = o.cpu().double().numpy(), sf.cpu().double().numpy()
+        print(f"segments={P}: max|O - one-kernel O| {float((o.float() - o1.float()).abs().max()):.3e}", flush=True)
+        assert _err(og, ro, f"segments={P} O vs chunked oracle") <= TOL
+        assert _err(sg, rs, f"segments={P} state vs chunked oracle") <= TOL
+        assert _err(og, to, f"segments={P} O vs token recurrence") <= 2 * TOL
+        assert _err(sg, ts, f"segments={P} state vs token recurrence") <= 2 * TOL
+
+
+def test_gdn_segmented_single_run_is_one_kernel():
+    """Asked for one run, or for runs on a one-chunk sequence, the segmented entry point runs the
+    one-kernel mode: the same bits, and no workspace needed."""
+    for T, P in ((300, 1), (64, 4), (10, 2)):
+        w, (q, k, v, g, beta, s0) = _case(1, T, 2, 4, 128, torch.bfloat16, True, seed=T)
+        dev = [t.cuda() for t in (q, k, v, g, beta, s0)]
+        o1, s1, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, two_kernel=False)
+        assert fa.gdn_segmented_workspace_size(1, T, 4, 128, P) == 0
+        o2, s2, _ = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, A=A, segments=P)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2), (T, P)

@@ -1,5 +1,5 @@
 """Every output element is written by every launch shape of the forward (O, lse), the backward (dq,
-dk, dv) and the Gated DeltaNet prefill (O, final state): the outputs are pre-filled with NaN (and,
+dk, dv) and the Gated DeltaNet prefill (O, final state; all three modes): the outputs are pre-filled with NaN (and,
 in a second call, with zeros), and the two results must be identical bit for bit and free of
 NaN.  The parity tests compare against the oracle, but a buffer that happens to hold an earlier
 call's correct values would hide an element a kernel never stores (one key group's half of the
@@ -118,5 +118,35 @@ def test_gdn_writes_every_output(two_kernel):
     (o_nan, sf_nan), (o_zero, sf_zero) = outs
     print(f"gdn two_kernel={two_kernel}: NaN in O {int(torch.isnan(o_nan).sum())}, in state "
           f"{int(torch.isnan(sf_nan).sum())}", flush=True)
+    assert not torch.isnan(o_nan).any() and not torch.isnan(sf_nan).any()
+    assert torch.equal(o_nan, o_zero) and torch.equal(sf_nan, sf_zero)
+
+
+def test_gdn_segmented_writes_every_output():
+    from gqa_attention_forward_amd.inputs import GdnWorkload, make_gdn_inputs
+
+    # 5 chunks (the last ragged) in runs of 2, 2 and 1: only the last run writes the final state
+    w = GdnWorkload("t", 2, 300, 2, 4, 128, 128, torch.bfloat16, 12, init_state=True)
+    q, k, v, g, beta, s0 = (t.cuda() for t in make_gdn_inputs(w))
+    _, _, A = fa.gdn_prefill(q, k, v, g, beta, s0=s0)
+    B, T, Hqk, DK = q.shape
+    Hv, DV = v.shape[2], v.shape[3]
+    ws_bytes = fa.gdn_segmented_workspace_size(B, T, Hv, DV, 3)
+    assert ws_bytes > 0
+    outs = []
+    for fill in (float("nan"), 0.0):
+        ws = torch.full((ws_bytes // 4,), fill, dtype=torch.float32, device=q.device)  # stale workspace too
+        o = torch.full((B, T, Hv, DV), fill, dtype=q.dtype, device=q.device)
+        sf = torch.full((B, Hv, DK, DV), fill, dtype=torch.float32, device=q.device)
+        rc = fa.gdn_chunk_fwd_segmented(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                                        A.data_ptr(), s0.data_ptr(), o.data_ptr(), sf.data_ptr(), B, T, Hqk, Hv, DK,
+                                        DV, 1.0 / math.sqrt(DK), fa.FA_BF16, 3, ws.data_ptr(), ws_bytes,
+                                        torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        outs.append((o, sf))
+    (o_nan, sf_nan), (o_zero, sf_zero) = outs
+    print(f"gdn segmented: NaN in O {int(torch.isnan(o_nan).sum())}, in state {int(torch.isnan(sf_nan).sum())}",
+          flush=True)
     assert not torch.isnan(o_nan).any() and not torch.isnan(sf_nan).any()
     assert torch.equal(o_nan, o_zero) and torch.equal(sf_nan, sf_zero)

@@ -179,3 +179,44 @@ def test_gdn_random(case):
         err = np.abs(gt - r).max()
         print(f"case {i} {name}: max|err| {err:.3e}, rel {err / m:.2e}", flush=True)
         assert np.all(np.isfinite(gt)) and err <= tol * m, name
+
+
+def _gdn_seg_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hqk = int(rng.integers(1, 3))
+        Hv = Hqk * int(rng.integers(1, 4))
+        T = int(rng.integers(65, 1500))
+        DV = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 3))
+        dtype = torch.float16 if rng.random() < 0.5 else torch.bfloat16
+        init = bool(rng.random() < 0.5)
+        lo = float(rng.choice([0.9, 0.99, 0.999, 1.0]))
+        runs = int(rng.integers(2, (T + 63) // 64 + 3))
+        cases.append((B, T, Hqk, Hv, DV, dtype, init, lo, runs, i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _gdn_seg_cases(8, 20254),
+                         ids=lambda c: f"{c[9]}-{'x'.join(str(x) for x in c[:5])}-{str(c[5]).split('.')[-1]}"
+                                       f"-s0{int(c[6])}-a{c[7]}-runs{c[8]}")
+def test_gdn_segmented_random(case):
+    """The segmented mode on random shapes, gates (U(lo, lo + (1 - lo))) and run counts (up to two
+    more than the chunks), against the oracle's chunk recurrence on the GPU's A."""
+    B, T, Hqk, Hv, DV, dtype, init, lo, runs, i = case
+    w = GdnWorkload("rand", B, T, Hqk, Hv, 128, DV, dtype, 5000 + i, init_state=init, gate_lo=lo,
+                    gate_span=1.0 - lo)
+    q, k, v, g, beta, s0 = make_gdn_inputs(w)
+    dev = [t.cuda() if t is not None else None for t in (q, k, v, g, beta, s0)]
+    o, sf, A = fa.gdn_prefill(*dev[:5], s0=dev[5], scale=w.scale, segments=runs)
+    torch.cuda.synchronize()
+    valid = np.arange(64)[None, :] <= (np.minimum(64, T - (np.arange(T) // 64) * 64) - 1)[:, None]
+    A_used = A.cpu().double().numpy() * valid[None, :, None, :]
+    ro, rs = oracle.gdn_chunked(q, k, v, g, beta, A_used, w.scale, s0)
+    for name, gt, r in (("O", o, ro), ("state", sf, rs)):
+        gt = gt.cpu().double().numpy()
+        m = max(1.0, np.abs(r).max())
+        err = np.abs(gt - r).max()
+        print(f"segmented case {i} {name}: max|err| {err:.3e}, rel {err / m:.2e}", flush=True)
+        assert np.all(np.isfinite(gt)) and err <= 5e-3 * m, name
