@@ -44,7 +44,7 @@
  *   gdn_chunk_workspace_size returns that size (0 for a non-positive argument).
  * gdn_chunk_plan: the sequential mode this library would pick for the shape: *workspace_bytes =
  *   the workspace size when the two-kernel mode is expected to be faster (its state walk then
- *   occupies at most half of the 256 CUs), else 0 (one kernel).  FA_ERR_INVALID_ARG for a null
+ *   occupies at most a quarter of the 256 CUs), else 0 (one kernel).  FA_ERR_INVALID_ARG for a null
  *   pointer or a non-positive size, FA_ERR_UNSUPPORTED for DV not a multiple of 64.
  * gdn_chunk_fwd_segmented: the same recurrence with the chunks cut into runs that are walked in
  *   parallel.  The recurrence is affine in the state, S_end = M S_start + Z for a run (M the run's

@@ -237,11 +237,12 @@ def test_gdn_workspace_size_and_check():
 
 
 def test_gdn_chunk_plan():
-    # two-kernel mode while the state walk (B * Hv * DV / 64 workgroups) fills at most 128 CUs
+    # two-kernel mode while the state walk (B * Hv * DV / 64 workgroups) fills at most 64 CUs
     assert fa.gdn_chunk_plan(1, 32768, 16, 128) == fa.gdn_chunk_workspace_size(1, 32768, 16, 128)  # 32 walkers
-    assert fa.gdn_chunk_plan(2, 4096, 32, 128) == fa.gdn_chunk_workspace_size(2, 4096, 32, 128)    # 128
+    assert fa.gdn_chunk_plan(1, 4096, 32, 128) == fa.gdn_chunk_workspace_size(1, 4096, 32, 128)    # 64
+    assert fa.gdn_chunk_plan(2, 4096, 32, 128) == 0                                                # 128
     assert fa.gdn_chunk_plan(8, 4096, 32, 128) == 0                                                # 512
-    assert fa.gdn_chunk_plan(1, 100, 129, 64) == 0                                                 # 129
+    assert fa.gdn_chunk_plan(1, 100, 65, 64) == 0                                                  # 65
     with pytest.raises(fa.FaError):
         fa.gdn_chunk_plan(1, 64, 2, 96)
     with pytest.raises(fa.FaError):

@@ -91,3 +91,16 @@ def test_gdn_capture():
         return fa.gdn_prefill(q, k, v, g, beta, s0=s0, scale=w.scale)
 
     _capture_and_replay(fn, "gdn prefill")
+
+
+def test_gdn_segmented_capture():
+    # 16 chunks in 4 runs: transition walks, the start-state combine and the output walks replayed
+    w = GdnWorkload("graph", 1, 1000, 2, 4, 128, 128, torch.bfloat16, 75, init_state=True, gate_lo=0.999,
+                    gate_span=0.001)
+    q, k, v, g, beta, s0 = make_gdn_inputs(w, device="cuda")
+    assert fa.gdn_segmented_workspace_size(1, 1000, 4, 128, 4) > 0
+
+    def fn():
+        return fa.gdn_prefill(q, k, v, g, beta, s0=s0, scale=w.scale, segments=4)
+
+    _capture_and_replay(fn, "gdn prefill, segmented")
