@@ -38,6 +38,7 @@
 
 #include "fa.h"
 #include "fa_device.h"
+#include "fa_mfma_run.h"
 #include "fa_tiles.h"
 
 namespace fa {
@@ -291,23 +292,24 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + (long long)r0 * row_bytes), (short)0,
                                                  bytes, 0x00020000);
     };
-    auto load_k = [&](int t, int buf) {  // the group's tile t
+    // copy instruction i of the group's K (or V) tile t into buffer buf
+    auto load_k_one = [&](int t, int buf, int i) {
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kg, k_rs, t0 + KG * t + grp);
-        lds_u8 *dst = kb_ptr(buf);
+        const int j = wave_u + kWaves * i;
+        lds_load16(rs, (lds_void *)(K_INSTR % kWaves == 0 || j < K_INSTR ? kb_ptr(buf) + j * 1024 : sink), k_src[i]);
+    };
+    auto load_v_one = [&](int t, int buf, int i) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, v_rs, t0 + KG * t + grp);
+        const int j = wave_u + kWaves * i;
+        lds_load16(rs, (lds_void *)(V_INSTR % kWaves == 0 || j < V_INSTR ? vb_ptr(buf) + j * 1024 : sink), v_src[i]);
+    };
+    auto load_k = [&](int t, int buf) {  // the group's tile t
 #pragma unroll
-        for (int i = 0; i < KI; ++i) {
-            const int j = wave_u + kWaves * i;
-            lds_load16(rs, (lds_void *)(K_INSTR % kWaves == 0 || j < K_INSTR ? dst + j * 1024 : sink), k_src[i]);
-        }
+        for (int i = 0; i < KI; ++i) load_k_one(t, buf, i);
     };
     auto load_v = [&](int t, int buf) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vg, v_rs, t0 + KG * t + grp);
-        lds_u8 *dst = vb_ptr(buf);
 #pragma unroll
-        for (int i = 0; i < VI; ++i) {
-            const int j = wave_u + kWaves * i;
-            lds_load16(rs, (lds_void *)(V_INSTR % kWaves == 0 || j < V_INSTR ? dst + j * 1024 : sink), v_src[i]);
-        }
+        for (int i = 0; i < VI; ++i) load_v_one(t, buf, i);
     };
     // every load into LDS this wave issued has landed; a barrier then publishes them
     // (s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum)
@@ -424,7 +426,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     // probabilities of s_cur (overwritten in place); otherwise s_cur already holds them.
     // Returns the in-lane max of s_next (unmasked); adds this tile's row sum to psum.
     auto step = [&](auto qk_tag, int kbuf, int vbuf, f32x16 (&s_next)[KB], f32x16 (&s_cur)[KB], float mt_cur,
-                    float &psum) {
+                    float &psum, auto &&copy) {
         constexpr bool QK = decltype(qk_tag)::value;
         float mc = 0.f;  // m * c of tile t, set by the running-max update inside the sequence
         constexpr int J0 = QK ? 0 : NM;  // first MFMA of the sequence
@@ -444,16 +446,18 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         if constexpr (QK) __builtin_amdgcn_s_setprio(1);
         float mt = -INFINITY;
         u32x4 bop[2];
-#pragma unroll
-        for (int j = J0; j < 2 * NM; ++j) {
-            if (j == NM) __builtin_amdgcn_s_setprio(0);
-            if (j + RA < 2 * NM) a[(j + RA) % (RA + 1)] = read_op(j + RA, kp, vp);
-            if (j < NM) {
+        static_for<J0, 2 * NM>([&](auto jc) {  // every MFMA index a compile-time constant
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j == NM) __builtin_amdgcn_s_setprio(0);
+            if constexpr (j + RA < 2 * NM) a[(j + RA) % (RA + 1)] = read_op(j + RA, kp, vp);
+            if constexpr (j < NM) {
                 s_next[j % KB] = Elem<T>::mfma(a[j % (RA + 1)], qreg[j / KB], s_next[j % KB]);
+                if constexpr (j % 2 == 1 && j / 2 < LOADS_PER_TILE)  // next tiles' copies, when spread
+                    copy(std::integral_constant<int, j / 2>{});
                 // the running-max update of tile t (and the rare rescale of O) runs while the
                 // first score MFMAs of tile t+1 execute; the probabilities follow
-                if (j == NPRE - 1) mc = update_max(mt_cur);
-                if (j >= NPRE) {
+                if constexpr (j == NPRE - 1) mc = update_max(mt_cur);
+                if constexpr (j >= NPRE) {
                     constexpr int SLOTS = NM - NPRE;
 #pragma unroll
                     for (int pr = (j - NPRE) * (VALS / 2) / SLOTS; pr < (j - NPRE + 1) * (VALS / 2) / SLOTS; ++pr) {
@@ -465,18 +469,18 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
                         }
                     }
                 }
-                if (j == NM - 1) {  // P octet 0 is needed by the first value MFMA
+                if constexpr (j == NM - 1) {  // P octet 0 is needed by the first value MFMA
 #pragma unroll
                     for (int w = 0; w < 4; ++w) bop[0][w] = cvt(s_cur, 0, w);
                 }
             } else {
-                const int i = j - NM, g = i / DB;
-                if (!QK && i == 0) {
+                constexpr int i = j - NM, g = i / DB;
+                if constexpr (!QK && i == 0) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) bop[0][w] = cvt(s_cur, 0, w);
                 }
                 oacc[i % DB] = Elem<T>::mfma(a[j % (RA + 1)], bop[g % 2], oacc[i % DB]);
-                if (g + 1 < NG) {
+                if constexpr (g + 1 < NG) {
 #pragma unroll
                     for (int w = (i % DB) * CPM; w < (i % DB + 1) * CPM; ++w) bop[(g + 1) % 2][w] = cvt(s_cur, g + 1, w);
                 }
@@ -495,7 +499,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
                 asm volatile("" : "+v"(mt), "+v"(psum));  // keep both chains in place
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
         return mt;
     };
 
@@ -537,12 +541,28 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     // nxt.  With ph = t % 2, K_{t+1} and V_t are read from buffers 1 - ph and ph, and the copies
     // of K_{t+2} and V_{t+1} go to buffers ph and 1 - ph.  ph is a compile-time constant (the
     // loop below runs steps in pairs), so every buffer is a fixed LDS object.
+    //
+    // On the full-grid shape (one 8-wave workgroup per CU) the step's copy instructions go out one
+    // after every other score MFMA rather than all at the top of the step, where the eight waves'
+    // copies would queue behind each other in the CU's address unit while the matrix core idles.
+    // Small grids (two key groups, the key-split mode) keep them at the top, where the copies'
+    // lead matters more than their issue cost.
+    constexpr bool SPREAD = W == 8 && KG == 1 && !SPLIT;
+    static_assert(!SPREAD || LOADS_PER_TILE <= NM / 2, "one copy after every other score MFMA covers the tile");
     auto body = [&](auto ph_c, int t, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
         constexpr int ph = decltype(ph_c)::value;
-        load_k(t + 2, ph);  // rows past N (or a tile past the end) read as zero
-        load_v(t + 1, 1 - ph);
+        auto copy = [&](auto ic) {  // copy instruction i of K_{t+2} (i < KI) or V_{t+1}
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i < KI) load_k_one(t + 2, ph, i);
+            else load_v_one(t + 1, 1 - ph, i - KI);
+        };
+        if constexpr (!SPREAD) {
+            load_k(t + 2, ph);  // rows past N (or a tile past the end) read as zero
+            load_v(t + 1, 1 - ph);
+        }
         float psum = 0.f;
-        float mt = step(std::true_type{}, 1 - ph, ph, nxt, cur, mt_pending, psum);
+        float mt = SPREAD ? step(std::true_type{}, 1 - ph, ph, nxt, cur, mt_pending, psum, copy)
+                          : step(std::true_type{}, 1 - ph, ph, nxt, cur, mt_pending, psum, [](auto) {});
         l_part += psum;
         if (t0 + KG * (t + 1) + grp >= kr.n_full) mt = mask_max(t + 1, nxt);  // diagonal band / ragged tail
         mt_pending = mt;
@@ -565,7 +585,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
         const float mc = update_max(mt_pending);
         probs(s_cur, mc);
         float psum = 0.f;
-        step(std::false_type{}, 0, vb_cur, s_nxt, s_cur, -INFINITY, psum);
+        step(std::false_type{}, 0, vb_cur, s_nxt, s_cur, -INFINITY, psum, [](auto) {});
         l_part += psum;
     }
 
