@@ -41,7 +41,7 @@ if ROOT not in sys.path:
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRCS = [os.path.join(ROOT, "gqa_attention_forward_amd", "csrc", f)
-               for f in ("fa_fwd.hip", "fa_device.h", "fa_tiles.h")]
+               for f in ("fa_fwd.hip", "fa_device.h", "fa_tiles.h", "fa_mfma_run.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_kernel_long_causal_gqa_16k_traffic.md")
 
 

@@ -424,7 +424,7 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
 
     // One step.  QK: also compute the scores s_next of the next tile (from kbuf) and the
     // probabilities of s_cur (overwritten in place); otherwise s_cur already holds them.
-    // Returns the in-lane max of s_next (unmasked); adds this tile's row sum to psum.
+    // Returns the in-lane max of s_next (unmasked); sets psum to this tile's row sum (psum is 0 on entry).
     auto step = [&](auto qk_tag, int kbuf, int vbuf, f32x16 (&s_next)[KB], f32x16 (&s_cur)[KB], float mt_cur,
                     float &psum, auto &&copy) {
         constexpr bool QK = decltype(qk_tag)::value;
@@ -487,7 +487,8 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
 #pragma unroll
                 for (int e = 0; e < VPM; ++e) {
                     const int v = i * VPM + e;
-                    psum += s_cur[v / 16][v % 16];
+                    if (i == 0 && e == 0) psum = s_cur[v / 16][v % 16];  // (saves the add to 0)
+                    else psum += s_cur[v / 16][v % 16];
                 }
                 if constexpr (QK) {
 #pragma unroll
