@@ -123,12 +123,16 @@ template <int D, int ROWS> struct TileLoad {
     // rows [r0, r0 + ROWS) of the slab at base, valid rows < rows_valid
     __device__ __forceinline__ void issue(const void *base, int r0, int rows_valid, lds_u8 *dst, int wave) const
     {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) issue_one(base, r0, rows_valid, dst, wave, i);
+    }
+    // instruction i (< PER_WAVE) of the above alone
+    __device__ __forceinline__ void issue_one(const void *base, int r0, int rows_valid, lds_u8 *dst, int wave, int i) const
+    {
         const int rows = rows_valid - r0 < ROWS ? rows_valid - r0 : ROWS;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const char *)base + (long long)r0 * RB), (short)0, rows > 0 ? rows * RB : 0, 0x00020000);
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i)
-            lds_load16(rs, (lds_void *)(dst + (wave + 4 * i) * 1024), src + i * 4 * RPK * RB);
+        lds_load16(rs, (lds_void *)(dst + (wave + 4 * i) * 1024), src + i * 4 * RPK * RB);
     }
 };
 
@@ -219,10 +223,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
         const int buf = t & 1;
         wait_vm0();
         __syncthreads();  // tile t visible to all waves; every wave is done with tile t - 1
-        if (t + 1 < n_tiles) {
-            ld.issue(kg, (t + 1) * kTile, N, smem + (buf ^ 1) * TILE, wave);
-            ld.issue(vg, (t + 1) * kTile, N, smem + (2 + (buf ^ 1)) * TILE, wave);
-        }
+        // the copies of tile t + 1 go out one every few MFMAs of the S / dP run below rather than
+        // all at once here; past the last tile they get an empty range (zeros into the spare buffer)
+        const int n_next = t + 1 < n_tiles ? N : 0;
+        auto copy = [&](auto cc) {
+            constexpr int c = decltype(cc)::value, PW = TileLoad<D, kTile>::PER_WAVE;
+            if constexpr (c < PW) ld.issue_one(kg, (t + 1) * kTile, n_next, smem + (buf ^ 1) * TILE, wave, c);
+            else ld.issue_one(vg, (t + 1) * kTile, n_next, smem + (2 + (buf ^ 1)) * TILE, wave, c - PW);
+        };
         const lds_u8 *kt = smem + buf * TILE, *vt = smem + (2 + buf) * TILE;
         f32x16 s[2], dp[2];
 #pragma unroll
@@ -242,6 +250,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
                     s[kb] = Elem<T>::mfma(a, qreg[m / 4], s[kb]);
                 else
                     dp[kb] = Elem<T>::mfma(a, dreg[m / 4], dp[kb]);
+                constexpr int NC = 2 * TileLoad<D, kTile>::PER_WAVE, ST = 4 * KS / NC;  // copies, MFMAs per copy
+                static_assert(ST * NC == 4 * KS, "copies spread evenly over the run");
+                if constexpr (m % ST == 1) copy(std::integral_constant<int, m / ST>{});
             });
         // dS^T = P^T (dP^T - Delta); register r of block kb is key n0 + 32 kb + 8 (r/4) + 4 hh + r%4
         __builtin_amdgcn_s_setprio(0);
