@@ -58,6 +58,8 @@ SMALL = [
     (4, 64, 64, 260, 130, 64, False, torch.float16),
     (2, 128, 16, 513, 700, 128, True, torch.float16),
     (1, 256, 32, 256, 64, 64, True, torch.bfloat16),      # exactly one key tile per row
+    (2, 64, 16, 700, 1111, 128, False, torch.bfloat16),   # non-causal, 18 key tiles, ragged last
+    (1, 128, 16, 1000, 1999, 128, True, torch.float16),   # 32 key tiles, bottom-right mask, ragged
     # more ragged small grids
     (5, 20, 4, 300, 400, 128, True, torch.float16),
     (1, 4, 2, 200, 200, 128, True, torch.bfloat16),
