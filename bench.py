@@ -510,6 +510,10 @@ def main():
                            "causal": w.causal, "seed": w.seed, "peaky_k_rows": w.peak_rate,
                            "parallelism": "single GPU"},
                 "pct_of_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 3),
+                # MFMA work the launch plan issues (whole tiles, including the masked parts of
+                # diagonal tiles), beside the algorithmic count the metric uses
+                "issued_mfma_tflop_per_step": round(issued / 1e12, 4),
+                "algorithmic_tflop_per_step": round(flops / 1e12, 4),
                 "step_ms": stats,
                 "roofline": roofline(w, flops, avg_ms, traffic),
                 "cpu_baseline": None,
