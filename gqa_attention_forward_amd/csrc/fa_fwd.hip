@@ -425,6 +425,8 @@ __device__ __forceinline__ void fa_fwd_body(const P &p)
     // One step.  QK: also compute the scores s_next of the next tile (from kbuf) and the
     // probabilities of s_cur (overwritten in place); otherwise s_cur already holds them.
     // Returns the in-lane max of s_next (unmasked); sets psum to this tile's row sum (psum is 0 on entry).
+    // copy(integral_constant<i>) is called after score MFMA 2 i + 1 for each of the step's copy
+    // instructions (a no-op where the caller issues the copies itself).
     auto step = [&](auto qk_tag, int kbuf, int vbuf, f32x16 (&s_next)[KB], f32x16 (&s_cur)[KB], float mt_cur,
                     float &psum, auto &&copy) {
         constexpr bool QK = decltype(qk_tag)::value;
