@@ -275,19 +275,13 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
 
 
-def attention_forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None,
-                      split_kv="auto"):
-    """O, lse = softmax(mask(q k^T * scale)) v for device tensors q [B,Hq,M,D], k/v [B,Hkv,N,D]
-    (fp16 or bf16) with unit stride along D and any other strides that keep rows 16-byte aligned
-    (e.g. [B,S,H,D] buffers passed as .transpose(1, 2) views).  Returns (o [B,Hq,M,D], lse
-    [B,Hq,M] fp32); a new `o` takes q's memory layout.
-
-    split_kv: "auto" runs the key-split forward when its plan splits some query tile (small
-    grids) or when M < 128 with grouped KV heads (the key-split kernel then stacks the query
-    heads of a group into one tile's rows), and fa_fwd otherwise; False always runs fa_fwd;
-    an int > 0 runs the key-split forward with at most that many key tiles per share.  The
-    split workspace comes from torch's caching allocator.  Kernels are enqueued on `stream`
-    (default: torch's current stream) and not waited for."""
+def forward_launcher(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None,
+                     split_kv="auto"):
+    """Checks and plans one forward the way attention_forward does (same arguments, same
+    dispatch) and returns (launch, out, lse): launch() enqueues that forward again with no
+    further checks or allocation (the key-split workspace, if any, is allocated here once and
+    kept by the closure).  For loops that run the same shapes many times; the tensors must stay
+    alive and keep their shapes."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -317,6 +311,9 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
     sts = [tuple(t.stride()[:3]) if strided else None for t in (q, k, v, out)]
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    lib = _load()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    dt = _dtype_code(q)
     if split_kv is not False:
         tiles = 0 if split_kv == "auto" else int(split_kv)
         if tiles < 0:
@@ -326,18 +323,42 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
             _, _, ws_bytes = fa_splitkv_plan(B, Hq, Hkv, M, N, D, causal, tiles)
             if ws_bytes > 0 or split_kv != "auto" or (M < 128 and Hq > Hkv):
                 ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
-                rc = fa_fwd_splitkv_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
-                                            Hq, Hkv, M, N, D, *sts, scale, causal, _dtype_code(q), tiles,
-                                            ws.data_ptr(), ws_bytes, stream)
-                if rc != FA_OK:
-                    raise FaError(rc, "fa_fwd_splitkv")
-                return out, lse
+                args = (*ptrs, B, Hq, Hkv, M, N, D, *[_st(x) for x in sts], float(scale), int(causal), dt,
+                        tiles, ws.data_ptr(), ws_bytes, stream)
+
+                def launch_split(_ws=ws):  # the closure keeps the workspace alive
+                    rc = lib.fa_fwd_splitkv_strided(*args)
+                    if rc != FA_OK:
+                        raise FaError(rc, "fa_fwd_splitkv")
+
+                return launch_split, out, lse
         elif split_kv != "auto":
             raise ValueError("the key-split forward needs D in (64, 128) and M <= 16384")
-    rc = fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, M, N,
-                        D, *sts, scale, causal, _dtype_code(q), stream)
-    if rc != FA_OK:
-        raise FaError(rc, "fa_fwd")
+    args = (*ptrs, B, Hq, Hkv, M, N, D, *[_st(x) for x in sts], float(scale), int(causal), dt, stream)
+
+    def launch():
+        rc = lib.fa_fwd_strided(*args)
+        if rc != FA_OK:
+            raise FaError(rc, "fa_fwd")
+
+    return launch, out, lse
+
+
+def attention_forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None,
+                      split_kv="auto"):
+    """O, lse = softmax(mask(q k^T * scale)) v for device tensors q [B,Hq,M,D], k/v [B,Hkv,N,D]
+    (fp16 or bf16) with unit stride along D and any other strides that keep rows 16-byte aligned
+    (e.g. [B,S,H,D] buffers passed as .transpose(1, 2) views).  Returns (o [B,Hq,M,D], lse
+    [B,Hq,M] fp32); a new `o` takes q's memory layout.
+
+    split_kv: "auto" runs the key-split forward when its plan splits some query tile (small
+    grids) or when M < 128 with grouped KV heads (the key-split kernel then stacks the query
+    heads of a group into one tile's rows), and fa_fwd otherwise; False always runs fa_fwd;
+    an int > 0 runs the key-split forward with at most that many key tiles per share.  The
+    split workspace comes from torch's caching allocator.  Kernels are enqueued on `stream`
+    (default: torch's current stream) and not waited for."""
+    launch, out, lse = forward_launcher(q, k, v, causal, scale, out, lse, stream, split_kv)
+    launch()
     return out, lse
 
 
@@ -461,5 +482,5 @@ __all__ = ["gdn_kkt", "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_chunk_pl
            "gdn_chunk_fwd_segmented", "gdn_segmented_workspace_size", "gdn_segment_plan",
            "fa_bwd", "fa_bwd_workspace_size", "attention_backward", "fa_fwd", "fa_fwd_strided",
            "fa_fwd_splitkv", "fa_fwd_splitkv_strided", "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES", "fa_splitkv_plan", "fa_strides",
-           "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward",
+           "fa_strerror", "fa_tile_shape", "fa_tile_counts", "fa_schedule", "attention_forward", "forward_launcher",
            "library", "FaError", "FA_F16", "FA_BF16", "LIB_PATH"]
