@@ -100,3 +100,18 @@ def test_respects_stream():
         o, lse = fa.attention_forward(q, k, v, causal=True, split_kv=False)
     s.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
+@pytest.mark.parametrize("split_kv", [False, "auto", 3])
+def test_forward_launcher_repeats_attention_forward(split_kv):
+    """A launcher planned once gives, launch after launch, the bits attention_forward gives for
+    the same call (plain and key-split paths; the split workspace lives in the launcher)."""
+    q, k, v = make_custom(1, 8, 2, 77, 3000, 128, torch.float16, seed=4, device="cuda")
+    o_ref, l_ref = fa.attention_forward(q, k, v, causal=True, split_kv=split_kv)
+    launch, o, lse = fa.forward_launcher(q, k, v, causal=True, split_kv=split_kv)
+    for _ in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        launch()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
