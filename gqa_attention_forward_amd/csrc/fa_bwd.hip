@@ -10,7 +10,7 @@
 //
 // Three kernels, all on the 32x32x16 MFMA with fp32 accumulation:
 //   prep:  Delta_i and lse_i * log2(e) per row, into a small workspace.
-//   dQ:    one workgroup per (b, h, 128 query rows), lane = query (as in the forward): per
+//   dQ:    one workgroup per (b, h, 128 or 256 query rows), lane = query (as in the forward): per
 //          64-key tile, S^T = K Q^T and dP^T = V dO^T with Q and dO resident in registers,
 //          dS^T from them, then dQ^T += K^T dS^T with K^T read by the transposing LDS read.
 //   dK/dV: one workgroup per (b, kv head, 128 keys), lane = key, K resident in registers and
@@ -46,7 +46,8 @@ namespace bwd {
 
 constexpr int kReadAhead = 3;  // LDS operand reads in flight ahead of the MFMA that uses them (mfma_run)
 
-constexpr int kRows = 128;  // rows a workgroup owns (4 waves x 32)
+constexpr int kRows = 128;  // rows a 4-wave workgroup owns (4 waves x 32)
+constexpr int kDqFullGrid = 256;  // 8-wave dQ workgroups that fill the MI355X's 256 CUs once
 constexpr int kTile = 64;   // rows of the inner-loop tile
 constexpr int kStats = 2 * kTile;  // floats per 64-row stats chunk: lse * log2(e), then Delta
 
@@ -103,17 +104,18 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p)
 // ------------------------------------------------------------ tile loads
 
 // HBM -> LDS copy of ROWS rows of a contiguous [rows, D] slab into the swizzled layout:
-// instruction j (of TI) fills LDS bytes [1 KiB j, 1 KiB (j+1)); the wave issues j = wave + 4 i.
-// Lane l's slot is row j * RPK + l / UPR, physical unit l % UPR; it gathers the logical unit
-// (l % UPR) ^ swz(row).  swz depends only on row bits that j = wave + 4 i does not change, so
-// one source offset per lane serves every i (plus i * 4 RPK rows).
-template <int D, int ROWS> struct TileLoad {
+// instruction j (of TI) fills LDS bytes [1 KiB j, 1 KiB (j+1)); of a workgroup of WV waves (4 or
+// 8) the wave issues j = wave + WV i.  Lane l's slot is row j * RPK + l / UPR, physical unit
+// l % UPR; it gathers the logical unit (l % UPR) ^ swz(row).  swz depends only on row bits that
+// j = wave + WV i does not change, so one source offset per lane serves every i (plus i WV RPK
+// rows).
+template <int D, int ROWS, int WV = 4> struct TileLoad {
     static constexpr int RB = 2 * D;                // bytes per row
     static constexpr int UPR = RB / 16;             // units per row
     static constexpr int RPK = 1024 / RB;           // rows per 1 KiB instruction
     static constexpr int TI = ROWS * RB / 1024;     // instructions per tile
-    static constexpr int PER_WAVE = TI / 4;
-    static_assert(PER_WAVE * 4 == TI, "tile instructions split over 4 waves");
+    static constexpr int PER_WAVE = TI / WV;
+    static_assert(PER_WAVE * WV == TI, "tile instructions split evenly over the waves");
     unsigned src;
     __device__ TileLoad(int wave, int lane)
     {
@@ -132,7 +134,7 @@ template <int D, int ROWS> struct TileLoad {
         const int rows = rows_valid - r0 < ROWS ? rows_valid - r0 : ROWS;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)((const char *)base + (long long)r0 * RB), (short)0, rows > 0 ? rows * RB : 0, 0x00020000);
-        lds_load16(rs, (lds_void *)(dst + (wave + 4 * i) * 1024), src + i * 4 * RPK * RB);
+        lds_load16(rs, (lds_void *)(dst + (wave + WV * i) * 1024), src + i * WV * RPK * RB);
     }
 };
 
@@ -165,9 +167,10 @@ template <typename T> __device__ __forceinline__ void store16(T *dst, const f32x
 
 // -------------------------------------------------------------------- dQ
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
+template <typename T, int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void dq_kernel(Params p)
 {
+    constexpr int QR = 32 * W;  // query rows of the workgroup
     constexpr int KS = D / 16, DB = D / 32, TILE = kTile * 2 * D;
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[4 * TILE];  // K0 K1 V0 V1
     lds_u8 *smem = (lds_u8 *)smem_raw;
@@ -177,8 +180,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
     const TileCoord tc = logical_tile(xcd_remap(blockIdx.x, p.gm), p.gm, CAUSAL);
     const int g = p.Hq / p.Hkv, hk = tc.h / g;
     const int M = p.M, N = p.N;
-    const int m0 = tc.qt * kRows;
-    const KvRange kr = kv_range(m0, kRows, kTile, M, N, CAUSAL);
+    const int m0 = tc.qt * QR;
+    const KvRange kr = kv_range(m0, QR, kTile, M, N, CAUSAL);
     const size_t bh = (size_t)tc.b * p.Hq + tc.h;
     const T *kg = (const T *)p.k + ((size_t)tc.b * p.Hkv + hk) * (size_t)N * D;
     const T *vg = (const T *)p.v + ((size_t)tc.b * p.Hkv + hk) * (size_t)N * D;
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    const TileLoad<D, kTile> ld(wave, lane);
+    const TileLoad<D, kTile, W> ld(wave, lane);
     const TrOffsets<D> tro(lane);
     const int n_tiles = kr.n_tiles;
     if (n_tiles > 0) {
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
         // all at once here; past the last tile they get an empty range (zeros into the spare buffer)
         const int n_next = t + 1 < n_tiles ? N : 0;
         auto copy = [&](auto cc) {
-            constexpr int c = decltype(cc)::value, PW = TileLoad<D, kTile>::PER_WAVE;
+            constexpr int c = decltype(cc)::value, PW = TileLoad<D, kTile, W>::PER_WAVE;
             if constexpr (c < PW) ld.issue_one(kg, (t + 1) * kTile, n_next, smem + (buf ^ 1) * TILE, wave, c);
             else ld.issue_one(vg, (t + 1) * kTile, n_next, smem + (2 + (buf ^ 1)) * TILE, wave, c - PW);
         };
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(Params p)
                     s[kb] = Elem<T>::mfma(a, qreg[m / 4], s[kb]);
                 else
                     dp[kb] = Elem<T>::mfma(a, dreg[m / 4], dp[kb]);
-                constexpr int NC = 2 * TileLoad<D, kTile>::PER_WAVE, ST = 4 * KS / NC;  // copies, MFMAs per copy
+                constexpr int NC = 2 * TileLoad<D, kTile, W>::PER_WAVE, ST = 4 * KS / NC;  // copies, MFMAs per copy
                 static_assert(ST * NC == 4 * KS, "copies spread evenly over the run");
                 if constexpr (m % ST == 1) copy(std::integral_constant<int, m / ST>{});
             });
@@ -480,14 +483,25 @@ static hipError_t launch_d(Params p, bool causal, hipStream_t s)
     hipLaunchKernelGGL((prep_kernel<T, D>), dim3((unsigned)chunks), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // dQ: 8 waves over 256 rows (one K/V tile copy serves twice the rows) when those workgroups
+    // alone fill every CU once at D = 128, else 4 waves over 128 rows
+    const bool w8 = D == 128 && (long long)p.B * p.Hq * ((p.M + 255) / 256) >= kDqFullGrid;
+    const int q_rows = w8 ? 256 : 128;
     Params pq = p;
-    pq.n_qt = (p.M + kRows - 1) / kRows;
+    pq.n_qt = (p.M + q_rows - 1) / q_rows;
     pq.total = (long long)p.B * p.Hq * pq.n_qt;
     pq.gm = make_grid_map((unsigned)pq.total, p.Hq / p.Hkv, pq.n_qt, p.Hkv);
-    if (causal)
-        hipLaunchKernelGGL((dq_kernel<T, D, true>), dim3((unsigned)pq.total), dim3(256), 0, s, pq);
-    else
-        hipLaunchKernelGGL((dq_kernel<T, D, false>), dim3((unsigned)pq.total), dim3(256), 0, s, pq);
+    if (w8) {
+        if (causal)
+            hipLaunchKernelGGL((dq_kernel<T, D, true, 8>), dim3((unsigned)pq.total), dim3(512), 0, s, pq);
+        else
+            hipLaunchKernelGGL((dq_kernel<T, D, false, 8>), dim3((unsigned)pq.total), dim3(512), 0, s, pq);
+    } else {
+        if (causal)
+            hipLaunchKernelGGL((dq_kernel<T, D, true, 4>), dim3((unsigned)pq.total), dim3(256), 0, s, pq);
+        else
+            hipLaunchKernelGGL((dq_kernel<T, D, false, 4>), dim3((unsigned)pq.total), dim3(256), 0, s, pq);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     Params pk = p;
     pk.n_qt = (p.N + kRows - 1) / kRows;

@@ -66,6 +66,9 @@ SHAPES = [
     (3, 2, 1, 1, 1, 128, True, torch.float16),           # one query, one key
     (1, 2, 1, 1, 500, 64, True, torch.bfloat16),         # one query row
     (1, 8, 1, 512, 512, 128, True, torch.bfloat16),      # 8 query heads per KV head
+    # grids that fill the CUs with 8-wave (256-row) dQ workgroups, ragged in M and N
+    (2, 64, 8, 300, 333, 128, True, torch.bfloat16),
+    (1, 256, 32, 260, 200, 128, False, torch.float16),
 ]
 
 
